@@ -1,0 +1,224 @@
+"""Benchmark of the CSA lightning-indexer top-k on one MI355X.
+
+One step = one csa_indexer_topk call over the whole workload (every query
+row scored against every usable compressed key, chunked partition-merge
+top-k, sorted outputs), inputs already resident in HBM.  Default workload:
+S=65,536 queries, m=4 (T=16,384 compressed keys), H_I=64 heads, D_I=128,
+k=2048, bf16 inputs q, kc ~ N(0,1)/sqrt(D_I) and w ~ N(0,1)/sqrt(H_I) drawn
+from a fixed seed on the device.
+
+Prints one JSON line: pairs/s over the whole job, the score kernel against
+the bf16 MFMA roofline (its duration measured with HIP events recorded by the
+library around every launch on the call's stream), peak HBM, and the CPU
+oracle timed on a bounded sample of the same workload's rows on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import streaming_indexer_top_amd as csa  # noqa: E402
+from streaming_indexer_top_amd import inputs  # noqa: E402
+
+METRIC = "scored q-k pairs/s at S=65536 V4-Flash dims; MFMA util %; peak HBM GB"
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def pair_count(S, T, m, q_pos0=0):
+    i = np.arange(S, dtype=np.int64) + q_pos0
+    return int(np.minimum(T, (i + 1) // m).sum())
+
+
+def make_inputs(cfg_n, dev):
+    c = inputs.config(cfg_n)
+    S, T, H, D = c["S"], c["T"], c["H"], c["D"]
+    if cfg_n == 4:
+        q, w, kc = inputs.bf16_mixture(S, T, H, D, seed=cfg_n, device=dev)
+        dist = "q,w N(0,1) scaled; kc 64-component Gaussian mixture (spread 0.3)"
+    else:
+        q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=cfg_n, device=dev)
+        dist = "q,kc ~ N(0,1)/sqrt(D_I), w ~ N(0,1)/sqrt(H_I)"
+    return c, q, w, kc, dist
+
+
+def cpu_baseline(q, w, kc, m, k, S, T, target_s, max_rows, seed):
+    """Times the CPU oracle on sampled rows of the same workload."""
+    import oracle
+    oracle.build()
+    threads = len(os.sched_getaffinity(0))
+    kf = kc.float().cpu().numpy()
+
+    def run(rows):
+        rows = np.array(sorted(rows), dtype=np.int64)
+        rt = torch.from_numpy(rows).to(q.device)
+        qf = q[rt].float().cpu().numpy()
+        wf = w[rt].float().cpu().numpy()
+        t0 = time.perf_counter()
+        res = oracle.topk(qf, wf, kf, m, k, pos=rows, nthreads=threads)
+        dt = time.perf_counter() - t0
+        pairs = int(np.minimum(T, (rows + 1) // m).sum())
+        return rows, res, dt, pairs
+
+    probe = inputs.sample_rows(S, m, k, 64, seed)
+    _, _, dt0, pairs0 = run(probe)
+    rate = pairs0 / max(dt0, 1e-9)
+    mean_pairs = pair_count(S, T, m) / S
+    want = int(min(max_rows, max(64, target_s * rate / max(mean_pairs, 1.0))))
+    rows = inputs.sample_rows(S, m, k, want, seed)
+    rows, res, dt, pairs = run(rows)
+    return {
+        "value": pairs / dt,
+        "unit": "pairs/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d query rows of the same workload (boundary rows plus seeded uniform draws), "
+                  "%d valid pairs, %.2f s wall on %d host threads" % (len(rows), pairs, dt, threads),
+        "seconds": dt,
+        "extrapolated_full_s": pair_count(S, T, m) / (pairs / dt),
+    }, rows, res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload number 2..5")
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--budget", type=int, default=0, help="workspace budget in bytes")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-max-rows", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no "
+              "multi-GPU mode (requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    csa.load_library()
+
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_alloc = torch.cuda.memory_allocated(dev)
+    c, q, w, kc, dist = make_inputs(args.workload, dev)
+    S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    torch.cuda.synchronize()
+    gen_peak = torch.cuda.max_memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+
+    ws_bytes = csa.workspace_size(S, T, H, D, m, k, chunk_keys=args.chunk, key_tile=args.tile,
+                                  workspace_budget=args.budget)
+    workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+    score = torch.empty((S, k), dtype=torch.float32, device=dev)
+    kw = dict(chunk_keys=args.chunk, key_tile=args.tile, workspace_budget=args.budget,
+              workspace=workspace, out=(idx, score))
+
+    for _ in range(args.warmup):
+        csa.topk(q, w, kc, m, k, **kw)
+    torch.cuda.synchronize()
+    csa.profile_collect()  # drop anything recorded so far
+
+    csa.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        csa.topk(q, w, kc, m, k, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    csa.profile_enable(False)
+    prof = csa.profile_collect()
+
+    resident = (q.numel() * q.element_size() + w.numel() * w.element_size()
+                + kc.numel() * kc.element_size() + idx.numel() * 4 + score.numel() * 4)
+    peak = torch.cuda.max_memory_allocated(dev) - base_alloc
+    ms = (t1 - t0) * 1e3 / args.steps
+    P = pair_count(S, T, m)
+    flops = P * 2 * H * D
+    score_ms, score_n = prof["score"]
+    sel_ms, sel_n = prof["select"]
+    per_launch_ms = score_ms / max(score_n, 1)
+    flops_per_launch = flops / max(score_n / args.steps, 1)
+    achieved = flops_per_launch / (per_launch_ms * 1e-3) / 1e12 if score_n else 0.0
+
+    out = {
+        "metric": METRIC,
+        "value": P / (ms * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "csa_indexer_topk S=%d T=%d H_I=%d D_I=%d m=%d k=%d causal bf16, %s"
+                        % (S, T, H, D, m, k, dist),
+            "S": S, "T": T, "H_I": H, "D_I": D, "m": m, "k": k,
+            "chunk_keys": args.chunk or "auto", "key_tile": args.tile or "auto",
+            "valid_pairs": P,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": None,
+            "kernel": "score_bf16_kernel",
+            "launch_ms": per_launch_ms,
+            "launches_per_step": score_n / args.steps,
+            "flops_per_launch": flops_per_launch,
+        },
+        "mfma_util_pct": 100.0 * flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "kernel_ms_per_step": {"score": score_ms / args.steps, "select": sel_ms / args.steps},
+        "peak_hbm_gb": peak / 1e9,
+        "peak_hbm": {"total_gib": peak / 2 ** 30, "workspace_bytes": ws_bytes,
+                     "resident_inputs_outputs_gib": resident / 2 ** 30,
+                     "above_resident_gib": (peak - resident) / 2 ** 30,
+                     "input_generation_peak_gib": gen_peak / 2 ** 30,
+                     "avoided_fp32_score_tensor_gib": S * H * T * 4 / 2 ** 30},
+    }
+
+    if not args.no_cpu_baseline:
+        base, rows, (o_idx, o_sc) = cpu_baseline(q, w, kc, m, k, S, T, args.cpu_seconds,
+                                                 args.cpu_max_rows, args.workload)
+        out["cpu_baseline"] = {kk: base[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+        out["cpu_baseline"]["extrapolated_full_s"] = base["extrapolated_full_s"]
+        rt = torch.from_numpy(rows).to(dev)
+        g_idx = idx[rt].cpu().numpy()
+        n = np.minimum(T, (rows + 1) // m)
+        rec = []
+        for r in range(len(rows)):
+            cnum = int(min(n[r], k))
+            if cnum:
+                rec.append(len(np.intersect1d(g_idx[r, :cnum], o_idx[r, :cnum])) / cnum)
+        out["sample_recall"] = {"min": float(min(rec)), "mean": float(np.mean(rec)),
+                                "rows": len(rows)}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,159 @@
+/*
+ * csa_indexer.h -- C ABI of libcsa_indexer.so, the MI355X (gfx950) library
+ * for the Compressed Sparse Attention (CSA) lightning-indexer top-k.
+ *
+ * Operation (page "StreamIndex: Memory-Bounded Compressed Sparse Attention
+ * via Streaming Top-k", Abstract): the lightning indexer, a learned scoring
+ * projection over the compressed keys, scores every key for every query with
+ * H_I indexer heads, and the top-k keys are kept per query.  The page's point
+ * is that the public implementations build the whole [B,S,H_I,T] FP32 score
+ * tensor before the top-k, while a chunked partition-merge top-k never does.
+ * This library is such a partition-merge: it scores one chunk of keys for a
+ * batch of queries at a time, keeps each query's best k per chunk and merges
+ * them, so its scratch memory is bounded by the workspace the caller hands in
+ * and never grows with S*T.
+ *
+ * The page prints no formula; the library computes
+ *
+ *   score(i,j) = sum_{h<H_I} w[i,h] * max(q[i,h,:] . kc[j,:], 0)
+ *
+ * for every key j usable by query row i: with p = q_pos0 + i its absolute
+ * position, key j is usable iff (j+1)*m <= p+1, i.e. j < n(i) =
+ * min(T, floor((p+1)/m)) (m is the compression ratio).  Row i of the output
+ * holds its min(k, n(i)) best keys ordered by score descending, ties by key
+ * index ascending, followed by padding idx = -1, score = -inf.  Scores are
+ * fp32; a zero score is always +0.
+ *
+ * Memory: every pointer is a device pointer (HIP device memory of the current
+ * device) owned by the caller.  Tensors are dense and row-major:
+ *   q     [S][H_I][D_I]   dtype       (16-byte aligned)
+ *   w     [S][H_I]        dtype       (aligned to the element size)
+ *   kc    [T][D_I]        dtype       (16-byte aligned)
+ *   idx   [S][k]          int32       (4-byte aligned)
+ *   score [S][k]          float32     (4-byte aligned)
+ *   workspace             bytes       (256-byte aligned)
+ * Outputs are fully overwritten, padding included, and must not overlap the
+ * inputs or the workspace.  The library allocates no device memory and keeps
+ * no state between calls (apart from the optional profiling counters below).
+ *
+ * Asynchrony: all device work is enqueued on `stream` (a hipStream_t; NULL is
+ * the default stream) and the call returns without waiting.  Results are
+ * ready when the stream reaches that point.  Asynchronous device faults show
+ * up at the caller's next synchronisation, not as a status here.
+ *
+ * Errors: functions return a csa status (0 = CSA_OK).  Every argument check
+ * runs before any HIP call, so a call that fails a check enqueues nothing.
+ * Inputs must be finite; NaN or Inf inputs are not detected and give
+ * unspecified (but memory-safe) results.
+ */
+#ifndef CSA_INDEXER_H
+#define CSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+/* Status codes. */
+#define CSA_OK 0
+#define CSA_ERR_NULL_PTR 1            /* a required pointer is NULL */
+#define CSA_ERR_BAD_SHAPE 2           /* negative size, H_I/D_I/m/k out of range */
+#define CSA_ERR_BAD_DTYPE 3           /* dtype is not CSA_F32 or CSA_BF16 */
+#define CSA_ERR_MISALIGNED 4          /* a pointer breaks the alignment above */
+#define CSA_ERR_WORKSPACE_TOO_SMALL 5 /* workspace_bytes below what one query block needs */
+#define CSA_ERR_UNSUPPORTED 6         /* valid request outside what this build implements */
+#define CSA_ERR_HIP 7                 /* a HIP call or kernel launch failed */
+#define CSA_ERR_BAD_OPTION 8          /* a field of csa_opts is out of range */
+
+/* Input dtypes (q, w and kc share one). */
+#define CSA_F32 0  /* IEEE fp32 */
+#define CSA_BF16 1 /* bfloat16; products are exact in fp32, sums are fp32 */
+
+/* Supported ranges of this build. */
+#define CSA_MAX_HEADS 64
+#define CSA_MAX_K 2048
+
+/*
+ * Tuning options; a zero field (or a NULL pointer to the struct) means
+ * "choose automatically".  Options change speed and workspace size only:
+ * for a given input the outputs are bit-identical for every setting.
+ */
+typedef struct csa_opts {
+    /* Keys per partition chunk: each query keeps its best k of every chunk
+     * and merges them into a running list.  A multiple of 256, or 0. */
+    int64_t chunk_keys;
+    /* Keys staged in LDS per step of the score kernel: 64, 128, 256, or 0. */
+    int32_t key_tile;
+    int32_t reserved0; /* must be 0 */
+    /* Upper bound, in bytes, on the workspace that
+     * csa_indexer_topk_workspace_size plans for; 0 means 1 GiB.  A smaller
+     * workspace only makes the library process fewer query rows per pass. */
+    int64_t workspace_budget;
+    int64_t reserved[4]; /* must be 0 */
+} csa_opts;
+
+/* CSA_ABI_VERSION of the built library. */
+int csa_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *csa_status_str(int status);
+
+/*
+ * Workspace bytes that csa_indexer_topk needs to process all S rows in as few
+ * passes as the budget allows.  Pure host arithmetic: no device access.
+ * Arguments as for csa_indexer_topk (q_pos0 included, since it decides how
+ * many keys the last row may use).  Writes the size to *bytes_out; the size is
+ * 0 when no row has a usable key.
+ */
+int csa_indexer_topk_workspace_size(int64_t S, int64_t T, int32_t H_I, int32_t D_I,
+                                    int32_t m, int64_t k, int64_t q_pos0, int32_t dtype,
+                                    const csa_opts *opts, size_t *bytes_out);
+
+/*
+ * The indexer top-k (see the top of this file for the operation, layouts and
+ * error behaviour).
+ *   q, w, kc      inputs, dtype `dtype`
+ *   S, T          query rows and compressed keys (>= 0; T < 2^31)
+ *   H_I           indexer heads, 1..CSA_MAX_HEADS
+ *   D_I           head dimension: 32, 64 or 128
+ *   m             compression ratio (>= 1)
+ *   k             keys kept per query, 1..CSA_MAX_K (k > T is fine: padding)
+ *   q_pos0        absolute position of row 0 (>= 0): lets a caller process a
+ *                 range of rows of a longer sequence
+ *   idx, score    outputs [S][k]
+ *   workspace     scratch device memory of workspace_bytes bytes; may be NULL
+ *                 when the size query returns 0.  Any size at least one query
+ *                 block's share works; larger ones need fewer passes.
+ *   opts          tuning options or NULL
+ *   stream        hipStream_t to enqueue on (NULL = default stream)
+ */
+int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype,
+                     int64_t S, int64_t T, int32_t H_I, int32_t D_I, int32_t m,
+                     int64_t k, int64_t q_pos0, int32_t *idx, float *score,
+                     void *workspace, size_t workspace_bytes, const csa_opts *opts,
+                     void *stream);
+
+/*
+ * Kernel timing for benchmarks.  While enabled, every kernel launch made by
+ * csa_indexer_topk on this process is bracketed by HIP events recorded on the
+ * launch's stream.  csa_profile_collect waits for those events, adds up the
+ * elapsed milliseconds and the launch counts per kernel kind into
+ * ms_out[kind] and launches_out[kind] for kind < n_kinds (either array may be
+ * NULL), then forgets them.  Not thread-safe; meant for single-threaded
+ * benchmark drivers.
+ */
+#define CSA_KERNEL_SCORE 0  /* chunk scoring: MFMA contraction + ReLU + head sum */
+#define CSA_KERNEL_SELECT 1 /* chunk top-k, merge into running lists, emit */
+#define CSA_KERNEL_KINDS 2
+int csa_profile_enable(int enable);
+int csa_profile_collect(double *ms_out, int64_t *launches_out, int32_t n_kinds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_INDEXER_H */

@@ -1,1 +1,9 @@
-"""MI355X-native Compressed Sparse Attention lightning-indexer top-k."""
+"""MI355X-native Compressed Sparse Attention lightning-indexer top-k.
+
+``topk`` scores every causally usable compressed key for each query with the
+lightning indexer and returns the query's top-k keys, through the C-ABI
+library ``libcsa_indexer.so`` and its gfx950 HIP kernels.  ``inputs`` holds
+the seeded synthetic input generators.
+"""
+from .binding import (CsaError, abi_version, library_path, load_library,  # noqa: F401
+                      profile_collect, profile_enable, topk, workspace_size)

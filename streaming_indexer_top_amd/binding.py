@@ -1,0 +1,185 @@
+"""Python binding of libcsa_indexer.so (argument marshalling only).
+
+Every step of the indexer runs in the library's HIP kernels; this module
+only checks tensor metadata, allocates outputs and workspace with PyTorch on
+the inputs' device, and passes raw pointers and torch's current HIP stream
+through ctypes.  If the library is missing or fails to load, every call
+raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcsa_indexer.so")
+
+CSA_F32 = 0
+CSA_BF16 = 1
+CSA_KERNEL_SCORE = 0
+CSA_KERNEL_SELECT = 1
+CSA_KERNEL_KINDS = 2
+KERNEL_NAMES = ("score", "select")
+
+EXPORTS = ("csa_abi_version", "csa_status_str", "csa_indexer_topk_workspace_size",
+           "csa_indexer_topk", "csa_profile_enable", "csa_profile_collect")
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("csa_indexer status %d: %s" % (status, msg))
+        self.status = status
+
+
+class csa_opts(ctypes.Structure):
+    _fields_ = [("chunk_keys", ctypes.c_int64),
+                ("key_tile", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32),
+                ("workspace_budget", ctypes.c_int64),
+                ("reserved", ctypes.c_int64 * 4)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: str | None = None):
+    """Load (once) and declare the C ABI."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libcsa_indexer.so not built at %s: run "
+                           "python -m streaming_indexer_top_amd.build" % p)
+    lib = ctypes.CDLL(p)
+    vp = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    lib.csa_abi_version.argtypes = []
+    lib.csa_abi_version.restype = ctypes.c_int
+    lib.csa_status_str.argtypes = [ctypes.c_int]
+    lib.csa_status_str.restype = ctypes.c_char_p
+    lib.csa_indexer_topk_workspace_size.argtypes = [i64, i64, i32, i32, i32, i64, i64, i32,
+                                                    ctypes.POINTER(csa_opts),
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+    lib.csa_indexer_topk_workspace_size.restype = ctypes.c_int
+    lib.csa_indexer_topk.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i64, i64,
+                                     vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(csa_opts), vp]
+    lib.csa_indexer_topk.restype = ctypes.c_int
+    lib.csa_profile_enable.argtypes = [ctypes.c_int]
+    lib.csa_profile_enable.restype = ctypes.c_int
+    lib.csa_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_int64), i32]
+    lib.csa_profile_collect.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().csa_status_str(status).decode()
+        raise CsaError(status, msg)
+
+
+def abi_version() -> int:
+    return load_library().csa_abi_version()
+
+
+def _opts(chunk_keys=0, key_tile=0, workspace_budget=0):
+    o = csa_opts()
+    o.chunk_keys = int(chunk_keys or 0)
+    o.key_tile = int(key_tile or 0)
+    o.workspace_budget = int(workspace_budget or 0)
+    return o
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return CSA_BF16
+    if t == torch.float32:
+        return CSA_F32
+    raise TypeError("q, w, kc must be bfloat16 or float32, got %s" % t)
+
+
+def workspace_size(S, T, H, D, m, k, *, q_pos0=0, dtype=torch.bfloat16, chunk_keys=0,
+                   key_tile=0, workspace_budget=0) -> int:
+    out = ctypes.c_size_t(0)
+    o = _opts(chunk_keys, key_tile, workspace_budget)
+    _check(load_library().csa_indexer_topk_workspace_size(
+        int(S), int(T), int(H), int(D), int(m), int(k), int(q_pos0), _dtype_code(dtype),
+        ctypes.byref(o), ctypes.byref(out)))
+    return int(out.value)
+
+
+def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
+         q_pos0: int = 0, chunk_keys: int = 0, key_tile: int = 0, workspace_budget: int = 0,
+         workspace: torch.Tensor | None = None, out: tuple | None = None):
+    """CSA lightning-indexer top-k on the GPU.
+
+    q [S, H, D], w [S, H], kc [T, D]: contiguous device tensors, all bfloat16
+    or all float32.  Returns (idx [S, k] int32, score [S, k] float32), rows
+    ordered by score descending then key index ascending, padded with -1 /
+    -inf.  Runs on torch's current stream; does not synchronise.
+    """
+    if q.dim() != 3 or w.dim() != 2 or kc.dim() != 2:
+        raise ValueError("q must be [S,H,D], w [S,H], kc [T,D]")
+    S, H, D = q.shape
+    T = kc.shape[0]
+    if tuple(w.shape) != (S, H) or (kc.shape[1] != D):
+        raise ValueError("shape mismatch: q %s, w %s, kc %s" % (tuple(q.shape), tuple(w.shape),
+                                                               tuple(kc.shape)))
+    if not (q.dtype == w.dtype == kc.dtype):
+        raise TypeError("q, w, kc must share one dtype")
+    dev = q.device
+    if dev.type != "cuda" or w.device != dev or kc.device != dev:
+        raise ValueError("q, w, kc must be on one GPU device")
+    for name, t in (("q", q), ("w", w), ("kc", kc)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    dt = _dtype_code(q.dtype)
+    lib = load_library()
+    o = _opts(chunk_keys, key_tile, workspace_budget)
+    if out is None:
+        idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+        score = torch.empty((S, k), dtype=torch.float32, device=dev)
+    else:
+        idx, score = out
+        if idx.shape != (S, k) or score.shape != (S, k) or idx.dtype != torch.int32 \
+                or score.dtype != torch.float32 or not idx.is_contiguous() \
+                or not score.is_contiguous():
+            raise ValueError("out must be contiguous int32/float32 tensors of shape [S, k]")
+    if workspace is None:
+        nbytes = workspace_size(S, T, H, D, m, k, q_pos0=q_pos0, dtype=q.dtype,
+                                chunk_keys=chunk_keys, key_tile=key_tile,
+                                workspace_budget=workspace_budget)
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        _check(lib.csa_indexer_topk(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+            ctypes.c_void_p(kc.data_ptr()), dt, S, T, H, D, int(m), int(k), int(q_pos0),
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(score.data_ptr()),
+            ctypes.c_void_p(workspace.data_ptr()), nbytes, ctypes.byref(o),
+            ctypes.c_void_p(stream)))
+    return idx, score
+
+
+def profile_enable(on: bool = True):
+    _check(load_library().csa_profile_enable(1 if on else 0))
+
+
+def profile_collect():
+    """{kernel name: (total ms, launches)} since the last collect; waits for
+    the recorded events."""
+    ms = (ctypes.c_double * CSA_KERNEL_KINDS)()
+    n = (ctypes.c_int64 * CSA_KERNEL_KINDS)()
+    _check(load_library().csa_profile_collect(ms, n, CSA_KERNEL_KINDS))
+    return {KERNEL_NAMES[i]: (ms[i], n[i]) for i in range(CSA_KERNEL_KINDS)}

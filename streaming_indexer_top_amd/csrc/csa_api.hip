@@ -1,0 +1,312 @@
+// C ABI and driver of libcsa_indexer.so: argument checks, workspace plan,
+// and the launch sequence of the chunked partition-merge.
+//
+// Plan (page "StreamIndex: Memory-Bounded Compressed Sparse Attention via
+// Streaming Top-k", Abstract: a chunked partition-merge top-k driver that
+// never materialises the [B,S,H_I,T] score tensor; the page sweeps chunk size
+// and key-tile size): the S query rows are processed in passes of R rows,
+// R chosen so that one pass's scratch fits the workspace.  Within a pass the
+// usable keys are cut into chunks of C keys.  For each chunk the score kernel
+// writes the pass's [R, C] head-reduced scores, then the select kernel folds
+// them into each row's running best-k list; the last chunk's select pass sorts
+// the lists and writes idx/score.  Scratch is R*(4C + 8k + 4) bytes, set by
+// the workspace and never by S*T.
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/csa_indexer.h"
+#include "csa_internal.h"
+
+namespace {
+
+constexpr int64_t kDefaultBudget = int64_t(1) << 30;
+constexpr int64_t kDefaultChunkCap = 32768;  // single chunk up to this many keys
+constexpr int64_t kDefaultChunk = 16384;
+constexpr int32_t kDefaultTile = 128;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int64_t n_max = 0;   // keys usable by the last row
+    int64_t chunk = 0;   // keys per chunk (0: no row has a key)
+    int64_t n_chunks = 0;
+    int32_t tile = kDefaultTile;
+    bool lists = false;  // more than one chunk: running lists live in the workspace
+};
+
+// Workspace bytes for a pass of `rows` rows.
+size_t pass_bytes(const Plan &p, int64_t rows, int64_t k)
+{
+    if (p.chunk == 0 || rows <= 0) return 0;
+    size_t b = align_up((size_t)rows * (size_t)p.chunk * sizeof(float));
+    if (p.lists) {
+        b += align_up((size_t)rows * (size_t)k * sizeof(uint64_t));
+        b += align_up((size_t)rows * sizeof(int32_t));
+    }
+    return b;
+}
+
+int check_args(int64_t S, int64_t T, int32_t H, int32_t D, int32_t m, int64_t k,
+               int64_t q_pos0, int32_t dtype, const csa_opts *opts)
+{
+    if (dtype != CSA_F32 && dtype != CSA_BF16) return CSA_ERR_BAD_DTYPE;
+    if (S < 0 || T < 0 || m < 1 || k < 1 || q_pos0 < 0 || H < 1) return CSA_ERR_BAD_SHAPE;
+    if (H > CSA_MAX_HEADS) return CSA_ERR_BAD_SHAPE;
+    if (D != 32 && D != 64 && D != 128) return CSA_ERR_BAD_SHAPE;
+    if (k > CSA_MAX_K) return CSA_ERR_UNSUPPORTED;
+    if (T > (int64_t)INT32_MAX - 1) return CSA_ERR_UNSUPPORTED;
+    if (S > ((int64_t)1 << 40) || q_pos0 > ((int64_t)1 << 40)) return CSA_ERR_UNSUPPORTED;
+    if (opts) {
+        if (opts->chunk_keys < 0 || (opts->chunk_keys % 256) != 0) return CSA_ERR_BAD_OPTION;
+        if (opts->key_tile != 0 && opts->key_tile != 64 && opts->key_tile != 128 &&
+            opts->key_tile != 256)
+            return CSA_ERR_BAD_OPTION;
+        if (opts->workspace_budget < 0 || opts->reserved0 != 0) return CSA_ERR_BAD_OPTION;
+        for (int i = 0; i < 4; ++i)
+            if (opts->reserved[i] != 0) return CSA_ERR_BAD_OPTION;
+    }
+    return CSA_OK;
+}
+
+Plan make_plan(int64_t S, int64_t T, int32_t m, int64_t q_pos0, const csa_opts *opts)
+{
+    Plan p;
+    p.n_max = S > 0 ? csa::n_usable(q_pos0 + S - 1, T, m) : 0;
+    if (opts && opts->key_tile) p.tile = opts->key_tile;
+    if (p.n_max == 0) return p;
+    const int64_t n_round = (p.n_max + 255) / 256 * 256;
+    int64_t c = (opts && opts->chunk_keys) ? opts->chunk_keys
+                                           : (n_round <= kDefaultChunkCap ? n_round : kDefaultChunk);
+    if (c > n_round) c = n_round;
+    p.chunk = c;
+    p.n_chunks = (p.n_max + c - 1) / c;
+    p.lists = p.n_chunks > 1;
+    return p;
+}
+
+// Rows per pass that fit `bytes` (0 if not even one query block fits).
+int64_t rows_fitting(const Plan &p, int64_t S, int64_t k, size_t bytes)
+{
+    if (pass_bytes(p, S, k) <= bytes) return S;
+    const size_t per_row = (size_t)p.chunk * 4 + (p.lists ? (size_t)k * 8 + 4 : 0);
+    int64_t r = (int64_t)(bytes / per_row);
+    r = r / csa::kScoreWaves * csa::kScoreWaves;
+    while (r > 0 && pass_bytes(p, r, k) > bytes) r -= csa::kScoreWaves;
+    return r;
+}
+
+// ---- optional per-kernel timing ----
+struct ProfRecord {
+    int kind;
+    hipEvent_t start, stop;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof_records;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event()
+{
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <class F>
+int launch_timed(int kind, hipStream_t s, F &&launch)
+{
+    ProfRecord rec{kind, nullptr, nullptr};
+    const bool prof = g_prof_on;
+    if (prof) {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        rec.start = prof_event();
+        rec.stop = prof_event();
+        if (rec.start) (void)hipEventRecord(rec.start, s);
+    }
+    hipError_t e = launch();
+    if (prof) {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        if (rec.stop) (void)hipEventRecord(rec.stop, s);
+        if (rec.start && rec.stop) g_prof_records.push_back(rec);
+    }
+    return e == hipSuccess ? CSA_OK : CSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char *csa_status_str(int status)
+{
+    switch (status) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case CSA_ERR_BAD_SHAPE: return "bad shape: sizes must be >= 0, 1 <= H_I <= 64, D_I in {32,64,128}, m >= 1, k >= 1";
+    case CSA_ERR_BAD_DTYPE: return "bad dtype: expected CSA_F32 or CSA_BF16";
+    case CSA_ERR_MISALIGNED: return "misaligned pointer";
+    case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small for one query block";
+    case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 2048 or T >= 2^31)";
+    case CSA_ERR_HIP: return "HIP call or kernel launch failed";
+    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256, key_tile one of 64/128/256, reserved fields 0";
+    default: return "unknown status";
+    }
+}
+
+int csa_indexer_topk_workspace_size(int64_t S, int64_t T, int32_t H_I, int32_t D_I, int32_t m,
+                                    int64_t k, int64_t q_pos0, int32_t dtype,
+                                    const csa_opts *opts, size_t *bytes_out)
+{
+    if (!bytes_out) return CSA_ERR_NULL_PTR;
+    int st = check_args(S, T, H_I, D_I, m, k, q_pos0, dtype, opts);
+    if (st != CSA_OK) return st;
+    const Plan p = make_plan(S, T, m, q_pos0, opts);
+    const int64_t budget = (opts && opts->workspace_budget) ? opts->workspace_budget : kDefaultBudget;
+    int64_t rows = rows_fitting(p, S, k, (size_t)budget);
+    const int64_t min_rows = S < csa::kScoreWaves ? S : csa::kScoreWaves;
+    if (rows < min_rows) rows = min_rows;
+    *bytes_out = pass_bytes(p, rows, k);
+    return CSA_OK;
+}
+
+int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype, int64_t S,
+                     int64_t T, int32_t H_I, int32_t D_I, int32_t m, int64_t k, int64_t q_pos0,
+                     int32_t *idx, float *score, void *workspace, size_t workspace_bytes,
+                     const csa_opts *opts, void *stream)
+{
+    int st = check_args(S, T, H_I, D_I, m, k, q_pos0, dtype, opts);
+    if (st != CSA_OK) return st;
+    if (S == 0) return CSA_OK;
+    const Plan p = make_plan(S, T, m, q_pos0, opts);
+    if (!q || !w || !idx || !score) return CSA_ERR_NULL_PTR;
+    if (p.n_max > 0 && !kc) return CSA_ERR_NULL_PTR;
+    const size_t esz = dtype == CSA_BF16 ? 2 : 4;
+    if (((uintptr_t)q & 15) || ((uintptr_t)kc & 15) || ((uintptr_t)w & (esz - 1)) ||
+        ((uintptr_t)idx & 3) || ((uintptr_t)score & 3) || ((uintptr_t)workspace & (kAlign - 1)))
+        return CSA_ERR_MISALIGNED;
+    int64_t rows = S;
+    if (p.chunk > 0) {
+        if (!workspace) return CSA_ERR_NULL_PTR;
+        rows = rows_fitting(p, S, k, workspace_bytes);
+        if (rows <= 0) return CSA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    hipStream_t s = (hipStream_t)stream;
+
+    char *wsb = (char *)workspace;
+    for (int64_t r0 = 0; r0 < S; r0 += rows) {
+        const int64_t nr = rows < S - r0 ? rows : S - r0;
+        const int64_t n_hi = csa::n_usable(q_pos0 + r0 + nr - 1, T, m);
+        const int64_t nch = (p.chunk > 0 && n_hi > 0) ? (n_hi + p.chunk - 1) / p.chunk : 1;
+        float *ws_scores = (float *)wsb;
+        uint64_t *lists = nullptr;
+        int32_t *counts = nullptr;
+        if (p.lists) {
+            const size_t o1 = align_up((size_t)nr * (size_t)p.chunk * sizeof(float));
+            lists = (uint64_t *)(wsb + o1);
+            counts = (int32_t *)(wsb + o1 + align_up((size_t)nr * (size_t)k * sizeof(uint64_t)));
+        }
+        for (int64_t c = 0; c < nch; ++c) {
+            const int64_t c0 = c * p.chunk;
+            if (n_hi > c0) {
+                csa::ScoreArgs sa;
+                sa.q = q;
+                sa.w = w;
+                sa.kc = kc;
+                sa.ws = ws_scores;
+                sa.row0 = r0;
+                sa.rows = nr;
+                sa.q_pos0 = q_pos0;
+                sa.T = T;
+                sa.c0 = c0;
+                sa.clen = p.chunk;
+                sa.H = H_I;
+                sa.m = m;
+                // Split the chunk's keys over grid.y so that small passes still
+                // give every CU several workgroups; spans are whole tiles and
+                // at least 2048 keys so q is loaded rarely.
+                const int64_t span_keys = (n_hi - c0 < p.chunk) ? n_hi - c0 : p.chunk;
+                const int64_t nqb = (nr + csa::kScoreWaves - 1) / csa::kScoreWaves;
+                int64_t ysplit = (2048 + nqb - 1) / nqb;
+                const int64_t ymax = (span_keys + 2047) / 2048;
+                if (ysplit > ymax) ysplit = ymax;
+                if (ysplit < 1) ysplit = 1;
+                int64_t kspan = (span_keys + ysplit - 1) / ysplit;
+                kspan = (kspan + p.tile - 1) / p.tile * p.tile;
+                ysplit = (span_keys + kspan - 1) / kspan;
+                sa.kspan = kspan;
+                st = launch_timed(CSA_KERNEL_SCORE, s, [&] {
+                    return csa::launch_score(sa, dtype, D_I, p.tile, ysplit, s);
+                });
+                if (st != CSA_OK) return st;
+            }
+            csa::SelectArgs se;
+            se.ws = ws_scores;
+            se.lists = lists;
+            se.counts = counts;
+            se.out_idx = idx;
+            se.out_score = score;
+            se.row0 = r0;
+            se.rows = nr;
+            se.q_pos0 = q_pos0;
+            se.T = T;
+            se.c0 = c0;
+            se.clen = p.chunk;
+            se.k = k;
+            se.m = m;
+            se.first = c == 0;
+            se.emit = c == nch - 1;
+            st = launch_timed(CSA_KERNEL_SELECT, s, [&] { return csa::launch_select(se, s); });
+            if (st != CSA_OK) return st;
+        }
+    }
+    return CSA_OK;
+}
+
+int csa_profile_enable(int enable)
+{
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    g_prof_on = enable != 0;
+    return CSA_OK;
+}
+
+int csa_profile_collect(double *ms_out, int64_t *launches_out, int32_t n_kinds)
+{
+    std::vector<ProfRecord> recs;
+    {
+        std::lock_guard<std::mutex> g(g_prof_mu);
+        recs.swap(g_prof_records);
+    }
+    for (int i = 0; i < n_kinds; ++i) {
+        if (ms_out) ms_out[i] = 0.0;
+        if (launches_out) launches_out[i] = 0;
+    }
+    int st = CSA_OK;
+    for (const ProfRecord &r : recs) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(r.stop) != hipSuccess ||
+            hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+            st = CSA_ERR_HIP;
+        if (r.kind >= 0 && r.kind < n_kinds) {
+            if (ms_out) ms_out[r.kind] += ms;
+            if (launches_out) launches_out[r.kind] += 1;
+        }
+    }
+    std::lock_guard<std::mutex> g(g_prof_mu);
+    for (const ProfRecord &r : recs) {
+        g_prof_pool.push_back(r.start);
+        g_prof_pool.push_back(r.stop);
+    }
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol its header
+declares, and rejects bad arguments before touching the GPU.  No call here
+reaches a kernel launch."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import streaming_indexer_top_amd as csa
+from streaming_indexer_top_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa_indexer.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(csa.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    lib = csa.load_library()
+    assert lib.csa_abi_version() == 1
+    for st in range(0, 10):
+        assert lib.csa_status_str(st)
+
+
+def _ws(S, T, H=64, D=128, m=4, k=2048, **kw):
+    return csa.workspace_size(S, T, H, D, m, k, **kw)
+
+
+def test_workspace_bounded_independent_of_sequence_length():
+    # The score tensor [S, H, T] at S = 2^20 would be 64 TiB; the workspace
+    # stays within the default 1 GiB budget at every size.
+    for S in (1 << 14, 1 << 16, 1 << 18, 1 << 20):
+        b = _ws(S, S // 4)
+        assert 0 < b <= (1 << 30)
+    assert _ws(1 << 20, 1 << 18, workspace_budget=256 << 20) <= 256 << 20
+
+
+def test_workspace_zero_without_usable_keys():
+    assert _ws(3, 100, m=4) == 0           # rows 0..2 see no key
+    assert _ws(100, 0) == 0                 # no keys
+    assert _ws(0, 100) == 0                 # no rows
+
+
+def test_workspace_single_chunk_when_small():
+    # 1024 rows, last row sees 256 keys: one chunk of 256 keys, no lists.
+    assert _ws(1024, 256, H=4, D=32, k=16) == 1024 * 256 * 4
+
+
+def test_workspace_tiny_budget_still_fits_one_block():
+    b = _ws(1 << 16, 1 << 14, workspace_budget=1)
+    assert b > 0
+    assert b <= 8 * (1 << 14) * 4 + 8 * 2048 * 8 + 1024
+
+
+def _call(lib, q=1, w=1, kc=1, dtype=1, S=8, T=8, H=4, D=32, m=4, k=2, q_pos0=0,
+          idx=1, score=1, ws=None, ws_bytes=0, opts=None):
+    P = ctypes.c_void_p
+    al = 4096  # a fake, suitably aligned address: every call here fails a check first
+    conv = lambda v: P(al * v if isinstance(v, int) and v in (0, 1) else v)
+    return lib.csa_indexer_topk(conv(q), conv(w), conv(kc), dtype, S, T, H, D, m, k, q_pos0,
+                                conv(idx), conv(score), P(ws), ws_bytes,
+                                ctypes.byref(opts) if opts is not None else None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), 3),
+    (dict(S=-1), 2),
+    (dict(T=-1), 2),
+    (dict(H=0), 2),
+    (dict(H=65), 2),
+    (dict(D=48), 2),
+    (dict(m=0), 2),
+    (dict(k=0), 2),
+    (dict(q_pos0=-3), 2),
+    (dict(k=4096), 6),
+    (dict(q=0), 1),
+    (dict(w=0), 1),
+    (dict(idx=0), 1),
+    (dict(score=0), 1),
+    (dict(kc=0), 1),
+    (dict(q=4096 + 8), 4),
+    (dict(kc=4096 + 4), 4),
+    (dict(score=4096 + 2), 4),
+    (dict(ws=None, ws_bytes=0), 1),  # keys exist, so a workspace is required
+])
+def test_argument_checks_fail_before_any_device_work(kw, status):
+    lib = csa.load_library()
+    assert _call(lib, **kw) == status
+
+
+def test_workspace_too_small():
+    lib = csa.load_library()
+    assert _call(lib, ws=4096 * 16, ws_bytes=64, S=4096, T=1024) == 5
+
+
+def test_bad_options():
+    lib = csa.load_library()
+    for field, val in (("chunk_keys", 100), ("key_tile", 96), ("workspace_budget", -1),
+                       ("reserved0", 1)):
+        o = binding.csa_opts()
+        setattr(o, field, val)
+        assert _call(lib, opts=o) == 8, field
+    o = binding.csa_opts()
+    o.reserved[2] = 1
+    assert _call(lib, opts=o) == 8
+
+
+def test_python_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros((4, 2, 32), dtype=torch.bfloat16)
+    w = torch.zeros((4, 2), dtype=torch.bfloat16)
+    kc = torch.zeros((3, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # CPU tensors: no silent CPU path
+        csa.topk(q, w, kc, 4, 2)
+    with pytest.raises(TypeError):
+        csa.topk(q, w.float(), kc, 4, 2)
+    with pytest.raises(ValueError):
+        csa.topk(q, w[:3], kc, 4, 2)

@@ -1,0 +1,259 @@
+"""GPU parity: libcsa_indexer.so (through its C ABI) against the CPU oracle.
+
+Integer-valued inputs are compared bit for bit (indices and score bits);
+float inputs by the tolerance rules in ``checks.py`` (2e-3 relative scores,
+threshold, min set recall 0.998).  Sizes run from tiny edge cases through
+several tiles with ragged tails to the full workload shapes, where the oracle
+checks a fixed sample of rows.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import checks
+import oracle
+import streaming_indexer_top_amd as csa
+from streaming_indexer_top_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_topk(q, w, kc, m, k, **kw):
+    idx, sc = csa.topk(q.to(DEV), w.to(DEV), kc.to(DEV), m, k, **kw)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def oracle_topk(q, w, kc, m, k, rows=None, q_pos0=0):
+    qf = q.float().cpu().numpy() if hasattr(q, "float") else q
+    wf = w.float().cpu().numpy() if hasattr(w, "float") else w
+    kf = kc.float().cpu().numpy() if hasattr(kc, "float") else kc
+    if rows is None:
+        return oracle.topk(qf, wf, kf, m, k, q_pos0=q_pos0)
+    rows = np.asarray(rows, dtype=np.int64)
+    return oracle.topk(qf[rows], wf[rows], kf, m, k, pos=rows + q_pos0)
+
+
+def assert_no_fail(fails):
+    assert not fails, "\n".join(fails[:10])
+
+
+# ---------------------------------------------------------------- tiny ----
+
+def test_tiny_fp32_gaussian():
+    c = inputs.config(1)
+    S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    q, w, kc = inputs.gaussian_fp32(S, T, H, D, seed=1)
+    say("tiny fp32 gaussian S=%d T=%d H=%d D=%d k=%d" % (S, T, H, D, k))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k)
+    fails, stats = checks.check_float(g_idx, g_sc, o_idx, o_sc, q.numpy(), w.numpy(),
+                                      kc.numpy(), np.arange(S), T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("signed_w", [False, True])
+def test_tiny_integer_bit_exact(dtype, signed_w):
+    c = inputs.config(1)
+    S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=1, dtype=dtype, signed_w=signed_w)
+    say("tiny integer %s signed_w=%s" % (dtype, signed_w))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+    assert_no_fail(checks.check_structure(g_idx, g_sc, np.arange(S), T, m, k))
+
+
+EDGE_CASES = [
+    # S, T, H, D, m, k, q_pos0
+    (1, 4, 4, 32, 4, 3, 0),       # one row, no usable key
+    (7, 3, 4, 32, 1, 5, 0),       # ragged query block, k > T
+    (37, 10, 5, 32, 1, 4, 0),     # m = 1
+    (50, 9, 3, 64, 5, 6, 0),      # m = 5, D = 64
+    (64, 16, 1, 32, 4, 2, 0),     # single head
+    (64, 16, 33, 128, 4, 8, 0),   # heads spill into a second 32-head block
+    (96, 200, 64, 128, 2, 20, 0),  # several key tiles, ragged tail
+    (40, 30, 8, 32, 4, 7, 100),   # row offset: rows see all 30 keys
+    (20, 0, 4, 32, 4, 5, 0),      # no keys at all
+    (300, 300, 16, 64, 1, 2048, 0),  # k beyond every row's key count
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", EDGE_CASES)
+def test_edge_cases_bit_exact(dtype, case):
+    S, T, H, D, m, k, q_pos0 = case
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=S + T, dtype=dtype, signed_w=True)
+    say("edge case %s %s" % (case, dtype))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
+def test_empty_query_set():
+    q = torch.zeros((0, 4, 32), dtype=torch.bfloat16)
+    w = torch.zeros((0, 4), dtype=torch.bfloat16)
+    kc = torch.zeros((8, 32), dtype=torch.bfloat16)
+    g_idx, g_sc = gpu_topk(q, w, kc, 4, 3)
+    assert g_idx.shape == (0, 3) and g_sc.shape == (0, 3)
+
+
+def test_signed_zero_scores_are_positive():
+    # Every head dot product is <= 0 and the weights are negative: every score
+    # is zero and must come out as +0, with ties broken by index.
+    S, T, H, D, m, k = 16, 4, 2, 32, 1, 3
+    q = torch.zeros((S, H, D), dtype=torch.bfloat16)
+    q[:, 0, 0] = -1.0
+    q[:, 1, 1] = -1.0
+    kc = torch.zeros((T, D), dtype=torch.bfloat16)
+    kc[:, 0] = 1.0
+    kc[:, 1] = 1.0
+    w = -torch.ones((S, H), dtype=torch.bfloat16)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+    assert not np.any(np.signbit(g_sc[g_idx >= 0]))
+
+
+# -------------------------------------------------------------- medium ----
+
+def test_medium_bf16_gaussian_full():
+    S, T, H, D, m, k = 4096, 1024, 64, 128, 4, 256
+    q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=2)
+    say("medium bf16 gaussian S=%d T=%d k=%d" % (S, T, k))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k)
+    fails, stats = checks.check_float(g_idx, g_sc, o_idx, o_sc, q.float().numpy(),
+                                      w.float().numpy(), kc.float().numpy(), np.arange(S),
+                                      T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
+def test_chunk_and_tile_grid_bit_identical():
+    """Integer inputs, rows far longer than a chunk: every chunk x tile
+    setting gives the same bits, equal to the oracle's."""
+    S, T, H, D, m, k = 1024, 3000, 64, 128, 1, 512
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=4, dtype=torch.bfloat16, signed_w=True)
+    q_pos0 = 2100  # rows see 2101..3000 keys
+    say("chunk/tile grid S=%d T=%d k=%d" % (S, T, k))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    for chunk in (0, 256, 768, 2048):
+        for tile in (64, 128, 256):
+            say("  chunk=%d tile=%d" % (chunk, tile))
+            g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, chunk_keys=chunk, key_tile=tile)
+            assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
+def test_small_workspace_many_passes():
+    S, T, H, D, m, k = 2000, 500, 8, 64, 4, 64
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=6, dtype=torch.bfloat16, signed_w=True)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k)
+    for budget, chunk in ((1, 0), (300 * 1024, 256), (5 << 20, 0)):
+        say("workspace budget %d chunk %d" % (budget, chunk))
+        g_idx, g_sc = gpu_topk(q, w, kc, m, k, workspace_budget=budget, chunk_keys=chunk)
+        assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
+def test_row_range_matches_full_run():
+    S, T, H, D, m, k = 3000, 750, 64, 128, 4, 128
+    q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=8)
+    full = gpu_topk(q, w, kc, m, k)
+    a, b = 1111, 2345
+    part = gpu_topk(q[a:b].contiguous(), w[a:b].contiguous(), kc, m, k, q_pos0=a)
+    assert np.array_equal(full[0][a:b], part[0])
+    assert np.array_equal(full[1][a:b].view(np.uint32), part[1].view(np.uint32))
+
+
+def test_scaling_keys_by_two_doubles_scores_exactly():
+    S, T, H, D, m, k = 2048, 512, 64, 128, 4, 64
+    q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=9)
+    a_idx, a_sc = gpu_topk(q, w, kc, m, k)
+    b_idx, b_sc = gpu_topk(q, w, (kc.float() * 2).to(torch.bfloat16), m, k)
+    assert np.array_equal(a_idx, b_idx)
+    assert np.array_equal(a_sc * 2, b_sc)
+
+
+def test_repeat_runs_bit_identical():
+    S, T, H, D, m, k = 4096, 1024, 64, 128, 4, 512
+    q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=10)
+    a = gpu_topk(q, w, kc, m, k)
+    b = gpu_topk(q, w, kc, m, k)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+# ------------------------------------------------- full workload shapes ----
+
+def _full_shape_check(cfg_n, kc_kind="gaussian", sample=None, integer=False, seed=None):
+    c = inputs.config(cfg_n)
+    S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    seed = cfg_n if seed is None else seed
+    say("config %d S=%d T=%d %s%s sample=%s" % (cfg_n, S, T, "integer " if integer else "",
+                                                kc_kind, sample))
+    gen_dev = DEV if S >= 65536 else "cpu"
+    if integer:
+        q, w, kc = inputs.integer_valued(S, T, H, D, seed=seed, dtype=torch.bfloat16,
+                                         signed_w=True, device=gen_dev)
+    elif kc_kind == "mixture":
+        q, w, kc = inputs.bf16_mixture(S, T, H, D, seed=seed, device=gen_dev)
+    else:
+        q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=seed, device=gen_dev)
+    q, w, kc = q.to(DEV), w.to(DEV), kc.to(DEV)
+    idx, sc = csa.topk(q, w, kc, m, k)
+    torch.cuda.synchronize()
+    rows = np.arange(S) if sample is None else np.array(inputs.sample_rows(S, m, k, sample, seed))
+    rows_t = torch.from_numpy(rows).to(DEV)
+    g_idx = idx[rows_t].cpu().numpy()
+    g_sc = sc[rows_t].cpu().numpy()
+    qf = q[rows_t].float().cpu().numpy()
+    wf = w[rows_t].float().cpu().numpy()
+    kf = kc.float().cpu().numpy()
+    del idx, sc, q, w
+    torch.cuda.empty_cache()
+    say("  gpu done, oracle on %d rows" % len(rows))
+    o_idx, o_sc = oracle.topk(qf, wf, kf, m, k, pos=rows)
+    if integer:
+        assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+        return
+    fails, stats = checks.check_float(g_idx, g_sc, o_idx, o_sc, qf, wf, kf, rows, T, m, k)
+    say("  stats %s" % stats)
+    assert_no_fail(fails)
+
+
+def test_cfg2_integer_bit_exact():
+    _full_shape_check(2, integer=True)
+
+
+def test_cfg2_bf16_all_rows():
+    _full_shape_check(2)
+
+
+def test_cfg3_bf16_sampled():
+    _full_shape_check(3, sample=4096)
+
+
+def test_cfg3_integer_sampled():
+    _full_shape_check(3, sample=1024, integer=True)
+
+
+@pytest.mark.slow
+def test_cfg4_mixture_sampled():
+    _full_shape_check(4, kc_kind="mixture", sample=1024)
+
+
+@pytest.mark.slow
+def test_cfg5_sampled():
+    _full_shape_check(5, sample=64)

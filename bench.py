@@ -102,6 +102,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-max-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="bytes of a plain device copy run once before timing, as a known "
+                         "reference for HBM traffic counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -130,6 +133,14 @@ def main():
     score = torch.empty((S, k), dtype=torch.float32, device=dev)
     kw = dict(chunk_keys=args.chunk, key_tile=args.tile, workspace_budget=args.budget,
               workspace=workspace, out=(idx, score))
+
+    if args.copy_probe:
+        src = torch.empty((args.copy_probe,), dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         csa.topk(q, w, kc, m, k, **kw)

@@ -9,8 +9,8 @@
 // usable keys are cut into chunks of C keys.  For each chunk the score kernel
 // writes the pass's [R, C] head-reduced scores, then the select kernel folds
 // them into each row's running best-k list; the last chunk's select pass sorts
-// the lists and writes idx/score.  Scratch is R*(4C + 8k + 4) bytes, set by
-// the workspace and never by S*T.
+// the lists and writes idx/score.  Scratch is R*(4C + 16 [+ 8k + 16]) bytes,
+// set by the workspace and never by S*T.
 #include <stdint.h>
 #include <string.h>
 
@@ -38,17 +38,28 @@ struct Plan {
     bool lists = false;  // more than one chunk: running lists live in the workspace
 };
 
-// Workspace bytes for a pass of `rows` rows.
-size_t pass_bytes(const Plan &p, int64_t rows, int64_t k)
+// Workspace layout of a pass of `rows` rows, in this order:
+//   scores [rows][chunk] fp32 | meta [rows] ChunkMeta |
+//   (more than one chunk:) lists [rows][k] u64 | state [rows] RowState
+struct PassLayout {
+    size_t meta, lists, state, end;
+};
+
+PassLayout pass_layout(const Plan &p, int64_t rows, int64_t k)
 {
-    if (p.chunk == 0 || rows <= 0) return 0;
-    size_t b = align_up((size_t)rows * (size_t)p.chunk * sizeof(float));
+    PassLayout l{0, 0, 0, 0};
+    if (p.chunk == 0 || rows <= 0) return l;
+    l.meta = align_up((size_t)rows * (size_t)p.chunk * sizeof(float));
+    l.end = l.meta + align_up((size_t)rows * sizeof(csa::ChunkMeta));
     if (p.lists) {
-        b += align_up((size_t)rows * (size_t)k * sizeof(uint64_t));
-        b += align_up((size_t)rows * sizeof(int32_t));
+        l.lists = l.end;
+        l.state = l.lists + align_up((size_t)rows * (size_t)k * sizeof(uint64_t));
+        l.end = l.state + align_up((size_t)rows * sizeof(csa::RowState));
     }
-    return b;
+    return l;
 }
+
+size_t pass_bytes(const Plan &p, int64_t rows, int64_t k) { return pass_layout(p, rows, k).end; }
 
 int check_args(int64_t S, int64_t T, int32_t H, int32_t D, int32_t m, int64_t k,
                int64_t q_pos0, int32_t dtype, const csa_opts *opts)
@@ -92,7 +103,8 @@ Plan make_plan(int64_t S, int64_t T, int32_t m, int64_t q_pos0, const csa_opts *
 int64_t rows_fitting(const Plan &p, int64_t S, int64_t k, size_t bytes)
 {
     if (pass_bytes(p, S, k) <= bytes) return S;
-    const size_t per_row = (size_t)p.chunk * 4 + (p.lists ? (size_t)k * 8 + 4 : 0);
+    const size_t per_row = (size_t)p.chunk * 4 + sizeof(csa::ChunkMeta) +
+                           (p.lists ? (size_t)k * 8 + sizeof(csa::RowState) : 0);
     int64_t r = (int64_t)(bytes / per_row);
     r = r / csa::kScoreWaves * csa::kScoreWaves;
     while (r > 0 && pass_bytes(p, r, k) > bytes) r -= csa::kScoreWaves;
@@ -199,6 +211,12 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
         if (!workspace) return CSA_ERR_NULL_PTR;
         rows = rows_fitting(p, S, k, workspace_bytes);
         if (rows <= 0) return CSA_ERR_WORKSPACE_TOO_SMALL;
+        // Same number of passes, rows spread evenly over them (a pass of a
+        // few rows would run on a handful of CUs).
+        const int64_t passes = (S + rows - 1) / rows;
+        int64_t even = (S + passes - 1) / passes;
+        even = (even + csa::kScoreWaves - 1) / csa::kScoreWaves * csa::kScoreWaves;
+        if (even < rows) rows = even;
     }
     hipStream_t s = (hipStream_t)stream;
 
@@ -207,14 +225,11 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
         const int64_t nr = rows < S - r0 ? rows : S - r0;
         const int64_t n_hi = csa::n_usable(q_pos0 + r0 + nr - 1, T, m);
         const int64_t nch = (p.chunk > 0 && n_hi > 0) ? (n_hi + p.chunk - 1) / p.chunk : 1;
+        const PassLayout lay = pass_layout(p, nr, k);
         float *ws_scores = (float *)wsb;
-        uint64_t *lists = nullptr;
-        int32_t *counts = nullptr;
-        if (p.lists) {
-            const size_t o1 = align_up((size_t)nr * (size_t)p.chunk * sizeof(float));
-            lists = (uint64_t *)(wsb + o1);
-            counts = (int32_t *)(wsb + o1 + align_up((size_t)nr * (size_t)k * sizeof(uint64_t)));
-        }
+        csa::ChunkMeta *meta = p.chunk > 0 ? (csa::ChunkMeta *)(wsb + lay.meta) : nullptr;
+        uint64_t *lists = p.lists ? (uint64_t *)(wsb + lay.lists) : nullptr;
+        csa::RowState *state = p.lists ? (csa::RowState *)(wsb + lay.state) : nullptr;
         for (int64_t c = 0; c < nch; ++c) {
             const int64_t c0 = c * p.chunk;
             if (n_hi > c0) {
@@ -223,6 +238,9 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
                 sa.w = w;
                 sa.kc = kc;
                 sa.ws = ws_scores;
+                sa.meta = meta;
+                sa.state = c > 0 ? state : nullptr;
+                sa.k = k;
                 sa.row0 = r0;
                 sa.rows = nr;
                 sa.q_pos0 = q_pos0;
@@ -231,28 +249,16 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
                 sa.clen = p.chunk;
                 sa.H = H_I;
                 sa.m = m;
-                // Split the chunk's keys over grid.y so that small passes still
-                // give every CU several workgroups; spans are whole tiles and
-                // at least 2048 keys so q is loaded rarely.
-                const int64_t span_keys = (n_hi - c0 < p.chunk) ? n_hi - c0 : p.chunk;
-                const int64_t nqb = (nr + csa::kScoreWaves - 1) / csa::kScoreWaves;
-                int64_t ysplit = (2048 + nqb - 1) / nqb;
-                const int64_t ymax = (span_keys + 2047) / 2048;
-                if (ysplit > ymax) ysplit = ymax;
-                if (ysplit < 1) ysplit = 1;
-                int64_t kspan = (span_keys + ysplit - 1) / ysplit;
-                kspan = (kspan + p.tile - 1) / p.tile * p.tile;
-                ysplit = (span_keys + kspan - 1) / kspan;
-                sa.kspan = kspan;
                 st = launch_timed(CSA_KERNEL_SCORE, s, [&] {
-                    return csa::launch_score(sa, dtype, D_I, p.tile, ysplit, s);
+                    return csa::launch_score(sa, dtype, D_I, p.tile, s);
                 });
                 if (st != CSA_OK) return st;
             }
             csa::SelectArgs se;
             se.ws = ws_scores;
+            se.meta = dtype == CSA_BF16 ? meta : nullptr;
             se.lists = lists;
-            se.counts = counts;
+            se.state = state;
             se.out_idx = idx;
             se.out_score = score;
             se.row0 = r0;

@@ -16,19 +16,51 @@ __host__ __device__ inline int64_t n_usable(int64_t pos, int64_t T, int32_t m)
     return n < T ? n : T;
 }
 
+// Per-row state kept between chunk passes: the running list's k-th key
+// (0 while the list holds fewer than k entries) and its length.
+struct RowState {
+    uint64_t theta;
+    int32_t count;
+    int32_t pad;
+};
+
+// Per-row summary of one chunk written by the score kernel: a histogram of
+// the orderable scores (top 11 bits) of the chunk keys that beat the row's
+// theta, reduced to the bin that holds the k-th best of them.
+struct ChunkMeta {
+    uint32_t bin;     // threshold bin b* (valid when total > k)
+    uint32_t above;   // entries in bins above b*
+    uint32_t in_bin;  // entries in bin b*
+    uint32_t total;   // entries counted (keys beating theta)
+};
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+
+// Monotone map of an fp32 score onto uint32 (-0 taken as +0): a larger
+// value means a larger score.
+__host__ __device__ inline uint32_t orderable(float s)
+{
+    uint32_t u;
+    __builtin_memcpy(&u, &s, 4);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // One pass of the score kernel: a batch of query rows against one key chunk.
 struct ScoreArgs {
     const void *q;    // [S][H][D], rows of this batch start at row0
     const void *w;    // [S][H]
     const void *kc;   // [T][D]
     float *ws;        // [rows][clen] head-reduced scores of this chunk
+    ChunkMeta *meta;  // [rows] chunk summary (bf16 path only; may be null)
+    const RowState *state;  // [rows] theta from earlier chunks, or null
+    int64_t k;
     int64_t row0;     // first q row of the batch
     int64_t rows;     // rows in the batch
     int64_t q_pos0;   // absolute position of q row 0
     int64_t T;
     int64_t c0;       // first key of the chunk
     int64_t clen;     // chunk length in keys; also the ws row stride
-    int64_t kspan;    // keys handled by one workgroup along grid.y
     int32_t H;
     int32_t m;
 };
@@ -36,8 +68,9 @@ struct ScoreArgs {
 // One pass of the select kernel over the same batch and chunk.
 struct SelectArgs {
     const float *ws;      // [rows][clen] scores written by the score pass
-    uint64_t *lists;      // [rows][k] running best-k lists (orderable keys)
-    int32_t *counts;      // [rows] entries in each running list
+    const ChunkMeta *meta;  // [rows] chunk summaries, or null (then no shortcut)
+    uint64_t *lists;      // [rows][k] running best-k lists, sorted descending
+    RowState *state;      // [rows] running list length and k-th key
     int32_t *out_idx;     // [S][k]
     float *out_score;     // [S][k]
     int64_t row0, rows, q_pos0, T;
@@ -51,10 +84,10 @@ struct SelectArgs {
 // Dtype codes as in the public header.
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
-// Score kernel: launches grid (ceil(rows/8) x ysplit) for bf16 or
-// (rows x ceil(clen/256)) for fp32.  `ysplit` is ignored for fp32.
+// Score kernel: grid ceil(rows/8) workgroups for bf16 (each covers the whole
+// chunk for its 8 rows) or (rows x ceil(clen/256)) for fp32.
 hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t key_tile,
-                        int64_t ysplit, hipStream_t stream);
+                        hipStream_t stream);
 
 // Select kernel: one workgroup per row of the batch.
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);

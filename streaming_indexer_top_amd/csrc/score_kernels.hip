@@ -13,13 +13,13 @@
 //
 // bf16 path: the contraction over the head dimension is a dense GEMM
 // [H_I, D_I] x [D_I, N] per query, run on the MFMA units with
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  A workgroup holds 8 query
+// v_mfma_f32_16x16x32_bf16 (fp32 accumulation).  A workgroup holds 8 query
 // rows, one per wave; each wave keeps its query's q fragments (64 heads x 128
 // dims = 64 VGPRs) and head weights resident and streams key tiles of NT keys
 // that the whole workgroup stages, double-buffered, through LDS.  In the
-// 32x32 accumulator layout a lane owns one key column and 16 head rows per
-// 32-head block, so the ReLU and the weighted head sum run in registers with
-// a single cross-half exchange at the end.
+// 16x16 accumulator layout a lane owns one key column and 4 heads per 16-head
+// block, so the ReLU and the weighted head sum run in registers, with two
+// cross-lane adds at the end.
 #include "csa_internal.h"
 
 namespace csa {
@@ -34,24 +34,65 @@ __device__ inline float bf16_bits_to_float(uint16_t b)
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// D: head dimension; HT: 32-head blocks (1 for H <= 32, else 2); NT: keys per
-// LDS tile.  Block = 8 waves, one query row each.  Grid: x = query blocks of
-// the batch (heaviest, i.e. latest, rows first), y = key spans of the chunk.
-template <int D, int HT, int NT>
+// Inverse of orderable(): the fp32 score of an orderable key.
+__device__ inline float key_score_of(uint32_t u)
+{
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// ReLU on the bit pattern: a float with the sign bit set is a negative
+// integer, so an integer max with 0 maps every negative score (and -0) to +0
+// and leaves the rest unchanged, in one instruction and with no NaN quieting.
+__device__ inline float relu_bits(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// D: head dimension; HT: 32-head blocks (ceil(H/32), at most 2); NT: keys
+// per LDS tile; DB: double-buffered tiles.  Block = 8 waves, one query row
+// each, covering the whole chunk for its rows.  Grid: query blocks of the
+// batch, heaviest (latest) rows first.
+//
+// MFMA shape: v_mfma_f32_32x32x16_bf16 with A = q (32 heads x 16 dims, held
+// in registers for the whole chunk) and B = kc (16 dims x 32 keys, read from
+// LDS).  The 32x32 shape keeps eight issue slots of matrix work per MFMA
+// instruction, which leaves the VALU room for the epilogue (MFMA and VALU
+// instructions share the issue port).  In the accumulator layout lane l owns
+// key column l%32 and 16 of each 32-head block's rows, so the ReLU and the
+// weighted head sum run in registers.
+//
+// Pipeline per 32-key block kb, in half-block steps (4 of the 8 k-steps):
+// the B fragments of the next step are read from LDS while the MFMAs of this
+// step run, and the VALU epilogue of block kb-1 is spread over the two steps
+// of block kb.  Blocks are finished in pairs: one 32-lane swap combines the
+// two halves of each block's head sum and leaves lane l with the score of key
+// 64*pair + l, so stores and histogram updates use all 64 lanes.
+//
+// Besides the scores, each wave builds an LDS histogram of its row's
+// orderable scores (top 11 bits) over the chunk keys that beat the row's
+// running k-th key theta, and at the end of the chunk reduces it to the bin
+// b* that holds the k-th best of those keys (ChunkMeta).  The select kernel
+// then only has to look at keys in bins >= b*.
+template <int D, int HT, int NT, bool DB>
 __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
 {
     constexpr int KSTEPS = D / 16;     // MFMA k-steps over the head dimension
+    constexpr int HALF = KSTEPS / 2;   // k-steps per pipeline step
     constexpr int CH = D / 8;          // 16-byte chunks per key row
     constexpr int ROWB = D * 2;        // bytes per key row
     constexpr int TILEB = NT * ROWB;   // bytes per LDS tile
-    constexpr int NCHUNK = NT * CH;    // 16-byte chunks per tile
-    constexpr int PER = (NCHUNK + 511) / 512;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * TILEB];
+    constexpr int NB = NT / 32;        // 32-key blocks per tile
+    constexpr int NBUF = DB ? 2 : 1;
+    static_assert(NB % 2 == 0, "blocks are finished in pairs");
+    // Dynamic LDS: [NBUF key tiles][8 row histograms].
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    unsigned char *lds = smem;
+    uint32_t *hist_all = (uint32_t *)(smem + NBUF * TILEB);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int half = lane >> 5;   // which 8-wide k slice / which 4-row group
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5;   // which 8-dim k slice (A, B) / which 4-row group (C)
     const int col = lane & 31;    // key column (B, C) or head row (A)
 
     const int64_t nqb = (a.rows + kScoreWaves - 1) / kScoreWaves;
@@ -60,56 +101,83 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
     const bool active = rl < a.rows;
     const int64_t last = min(qb * kScoreWaves + kScoreWaves - 1, a.rows - 1);
     const int64_t n_hi = n_usable(a.q_pos0 + a.row0 + last, a.T, a.m);
-    const int64_t kb0 = a.c0 + (int64_t)blockIdx.y * a.kspan;
-    const int64_t kcap = min(a.c0 + a.clen, kb0 + a.kspan);
+    const int64_t kb0 = a.c0;
+    const int64_t kcap = a.c0 + a.clen;
     const int64_t k_end = min(kcap, n_hi);
-    if (kb0 >= k_end) return;  // uniform over the workgroup
+    if (kb0 >= k_end) return;  // uniform: no row of this block has a key here
     const int64_t my_end =
         active ? min(kcap, n_usable(a.q_pos0 + a.row0 + rl, a.T, a.m)) : kb0;
     const int ntiles = (int)((k_end - kb0 + NT - 1) / NT);
 
-    // Resident A operand: q[row, ht*32 + col, ks*16 + half*8 .. +7].
+    // Keys must beat the row's running k-th key to matter; chunk keys come
+    // after every key already in the list, so on equal scores they lose and
+    // the test is on the score part alone.
+    uint32_t u_floor = 0;
+    bool filt = false;
+    if (active && a.state) {
+        const uint64_t th = a.state[rl].theta;
+        filt = th != 0;
+        u_floor = (uint32_t)(th >> 32);
+    }
+
+    for (int e = tid; e < kScoreWaves * kHistBins; e += 512) hist_all[e] = 0u;
+
+    // Resident A operand: q[row, ht*32 + col, ks*16 + half*8 .. +7], and the
+    // head weights of the accumulator rows this lane holds.  Every load is
+    // unconditional (rows and heads clamped to valid ones, results zeroed
+    // afterwards) so that all of them are in flight at once.
     bf16x8 qf[HT][KSTEPS];
     float wv[HT][16];
     {
         const int64_t row = a.row0 + (active ? rl : 0);
         const __bf16 *qrow = (const __bf16 *)a.q + row * (int64_t)a.H * D;
         const uint16_t *wrow = (const uint16_t *)a.w + row * (int64_t)a.H;
+        uint16_t wraw[HT][16];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            const int h = ht * 32 + col;
+            const int h = min(ht * 32 + col, a.H - 1);
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                bf16x8 v = {};
-                if (active && h < a.H)
-                    v = *(const bf16x8 *)(qrow + (int64_t)h * D + ks * 16 + half * 8);
-                qf[ht][ks] = v;
-            }
-            // Head row held by accumulator register r of this lane.
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                qf[ht][ks] = *(const bf16x8 *)(qrow + (int64_t)h * D + ks * 16 + half * 8);
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                wraw[ht][r] = wrow[min(ht * 32 + ((r >> 2) << 3) + (half << 2) + (r & 3), a.H - 1)];
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const bool hv = active && ht * 32 + col < a.H;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                if (!hv) qf[ht][ks] = bf16x8{};
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int hr = ht * 32 + ((r >> 2) << 3) + (half << 2) + (r & 3);
-                wv[ht][r] = (active && hr < a.H) ? bf16_bits_to_float(wrow[hr]) : 0.0f;
+                wv[ht][r] = (active && hr < a.H) ? bf16_bits_to_float(wraw[ht][r]) : 0.0f;
             }
         }
     }
 
     // Key tile staging: tile t holds keys kb0 + t*NT .. +NT-1, row-major with
-    // the 16-byte chunk index XOR-swizzled by the key so that the 32 lanes of
-    // a B-fragment read fall in distinct bank groups.
+    // the 16-byte chunk slot of chunk ch of key `key` at ch ^ (key % CH), so
+    // that the 16 lanes of each B-fragment read group fall in distinct bank
+    // groups.  The next tile is loaded into registers while the current one
+    // is computed and written to LDS after it.  (LDS DMA would save these
+    // registers, but then every LDS histogram update would wait for all
+    // outstanding global memory operations.)  Keys past the last usable one
+    // read a clamped (valid, unused) key.
+    constexpr int NCHUNK = NT * CH;                // 16-byte chunks per tile
+    constexpr int PER = (NCHUNK + 511) / 512;      // chunks per thread
     u32x4 st[PER];
     auto gload = [&](int t) {
         const int64_t base = kb0 + (int64_t)t * NT;
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = p * 512 + tid;
+            const int c = min(p * 512 + tid, NCHUNK - 1);
             const int key = c / CH;
             const int ch = c % CH;
-            const int64_t gk = base + key;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < NCHUNK && gk < k_end)
-                v = *(const u32x4 *)((const uint16_t *)a.kc + gk * D + ch * 8);
-            st[p] = v;
+            int64_t gk = base + key;
+            gk = gk < k_end ? gk : k_end - 1;
+            st[p] = *(const u32x4 *)((const uint16_t *)a.kc + gk * D + ch * 8);
         }
     };
     auto lstore = [&](int buf) {
@@ -123,8 +191,65 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
             }
         }
     };
+    // B fragments of half-step hs (k-steps hs*HALF .. +HALF-1) of block kb.
+    auto load_b = [&](const unsigned char *tb, int kb, int hs, bf16x8 (&b)[HALF]) {
+        const int key = kb * 32 + col;
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+            const int ch = 2 * (hs * HALF + j) + half;
+            b[j] = *(const bf16x8 *)(tb + key * ROWB + ((ch ^ (key & (CH - 1))) << 4));
+        }
+    };
+    auto mfma_half = [&](const bf16x8 (&b)[HALF], int hs, f32x16 (&acc)[HT]) {
+#pragma unroll
+        for (int j = 0; j < HALF; ++j) {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                if (hs == 0 && j == 0)
+                    acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][0], b[0], f32x16{}, 0, 0, 0);
+                else
+                    acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][hs * HALF + j], b[j],
+                                                                      acc[ht], 0, 0, 0);
+            }
+        }
+    };
 
-    float *wsrow = a.ws + (active ? rl : 0) * a.clen - a.c0;
+    // Scores are stored and counted 64 keys at a time (2 blocks): chunk-
+    // relative 32-bit key offsets, one lane per key.
+    float *wsrow = a.ws + (active ? rl : 0) * a.clen;
+    const int my_len = (int)(my_end - kb0);  // keys of this row in the chunk
+    const float f_floor = filt ? key_score_of(u_floor) : 0.0f;
+    uint32_t *h = hist_all + wave * kHistBins;
+
+    // Per-lane share of one block, over register half rh (8 of the 16
+    // accumulator rows of each 32-head block): ReLU and weighted sum.
+    auto partial = [&](const f32x16 (&acc)[HT], int rh, float &s0, float &s1) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+            for (int r = rh * 8; r < rh * 8 + 8; ++r) {
+                if (ht & 1) s1 = fmaf(wv[ht][r], relu_bits(acc[ht][r]), s1);
+                else s0 = fmaf(wv[ht][r], relu_bits(acc[ht][r]), s0);
+            }
+        }
+    };
+    // Finishes blocks 2p and 2p+1 (pe, po: each lane's share of them).  The
+    // 32-lane swap pairs the two half-waves, so lane l ends with the score of
+    // key 64p + l, summed as (lanes 0-31 share) + (lanes 32-63 share).
+    // Branch-free, so that the tile stays one scheduling region: lanes past
+    // the row's last key store into unused slots of the row (tiles never run
+    // past the chunk, whose length is a multiple of NT) and add 0 to the
+    // histogram.
+    auto finish2 = [&](float pe, float po, int rel0) {
+        const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe), __float_as_uint(po),
+                                                        false, false);
+        const float sc = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+        const int rel = rel0 + lane;
+        const bool valid = rel < my_len;
+        wsrow[rel] = sc;
+        const uint32_t inc = (valid && (!filt || sc > f_floor)) ? 1u : 0u;
+        atomicAdd(&h[orderable(sc) >> (32 - kHistBits)], inc);
+    };
 
     gload(0);
     lstore(0);
@@ -132,43 +257,87 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
     for (int t = 0; t < ntiles; ++t) {
         const bool more = t + 1 < ntiles;
         if (more) gload(t + 1);
-        const int64_t base = kb0 + (int64_t)t * NT;
-        if (active && base < my_end) {
-            const unsigned char *tb = lds + (t & 1) * TILEB;
+        const int rel_t = t * NT;  // tile start relative to the chunk
+        if (active && rel_t < my_len) {
+            const unsigned char *tb = lds + (DB ? (t & 1) * TILEB : 0);
+            bf16x8 bb[2][HALF];
+            f32x16 acc[2][HT];
+            float pacc = 0.0f;  // share of the block being finished
+            float pe = 0.0f;    // share of the even block of the current pair
+            load_b(tb, 0, 0, bb[0]);
 #pragma unroll
-            for (int kb = 0; kb < NT / 32; ++kb) {
-                const int key = kb * 32 + col;
-                f32x16 acc[HT];
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x16{};
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const int ch = 2 * ks + half;
-                    const bf16x8 b =
-                        *(const bf16x8 *)(tb + key * ROWB + ((ch ^ (key & (CH - 1))) << 4));
-#pragma unroll
-                    for (int ht = 0; ht < HT; ++ht)
-                        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ht][ks], b, acc[ht],
-                                                                          0, 0, 0);
+            for (int step = 0; step < 2 * NB; ++step) {
+                const int kb = step >> 1, hs = step & 1;
+                if (step + 1 < 2 * NB)
+                    load_b(tb, (step + 1) >> 1, (step + 1) & 1, bb[(step + 1) & 1]);
+                // Keep the prefetch here, one step ahead of its use.
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_half(bb[step & 1], hs, acc[kb & 1]);
+                if (kb > 0) {  // half hs of block kb-1's epilogue, under block kb's MFMAs
+                    float s0 = 0.0f, s1 = 0.0f;
+                    partial(acc[(kb - 1) & 1], hs, s0, s1);
+                    pacc = hs == 0 ? s0 + s1 : pacc + (s0 + s1);
+                    if (hs == 1) {
+                        if (((kb - 1) & 1) == 0) pe = pacc;
+                        else finish2(pe, pacc, rel_t + (kb - 2) * 32);
+                    }
                 }
-                // ReLU and weighted head sum; this lane holds 16 of each
-                // 32-head block's rows for key `key`, the other half-wave the
-                // other 16.
+            }
+            {  // last block of the tile
                 float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s0 = fmaf(wv[0][r], fmaxf(acc[0][r], 0.0f), s0);
-                if constexpr (HT == 2) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s1 = fmaf(wv[1][r], fmaxf(acc[1][r], 0.0f), s1);
-                }
-                float s = s0 + s1;
-                s = s + __shfl_xor(s, 32);
-                const int64_t gk = base + key;
-                if (half == 0 && gk < my_end) wsrow[gk] = s;
+                partial(acc[(NB - 1) & 1], 0, s0, s1);
+                pacc = s0 + s1;
+                s0 = 0.0f;
+                s1 = 0.0f;
+                partial(acc[(NB - 1) & 1], 1, s0, s1);
+                pacc = pacc + (s0 + s1);
+                finish2(pe, pacc, rel_t + (NB - 2) * 32);
             }
         }
-        if (more) lstore((t + 1) & 1);
+        if (more) {
+            if constexpr (!DB) __syncthreads();  // single buffer: all reads done
+            lstore(DB ? ((t + 1) & 1) : 0);
+        }
         __syncthreads();
+    }
+
+    // Chunk summary: locate the bin that holds the k-th best counted key.
+    if (active && a.meta) {
+        constexpr int PERL = kHistBins / 64;
+        uint32_t mine = 0;
+#pragma unroll 8
+        for (int i = 0; i < PERL; ++i) mine += h[lane * PERL + i];
+        uint32_t incl = mine;  // sum over lanes >= this lane
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_down(incl, off);
+            if (lane + off < 64) incl += y;
+        }
+        const uint32_t total = __shfl(incl, 0);
+        const uint32_t need = (uint32_t)a.k;
+        ChunkMeta m = {0u, 0u, 0u, total};
+        if (total > need) {
+            const uint32_t above_lane = incl - mine;
+            const bool here = above_lane < need && need <= incl;
+            const uint64_t who = __ballot(here);
+            const int src = __builtin_ctzll(who);
+            if (lane == src) {
+                uint32_t above = above_lane;
+                for (int i = PERL - 1; i >= 0; --i) {
+                    const uint32_t c = h[lane * PERL + i];
+                    if (above + c >= need) {
+                        m.bin = (uint32_t)(lane * PERL + i);
+                        m.above = above;
+                        m.in_bin = c;
+                        break;
+                    }
+                    above += c;
+                }
+                a.meta[rl] = m;
+            }
+        } else if (lane == 0) {
+            a.meta[rl] = m;
+        }
     }
 }
 
@@ -207,16 +376,34 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a)
     a.ws[rl * a.clen + (gk - a.c0)] = s;
 }
 
+template <int D, int HT, int NT, bool DB>
+hipError_t launch_bf16_cfg(const ScoreArgs &a, dim3 grid, hipStream_t s)
+{
+    constexpr size_t lds = (DB ? 2 : 1) * (size_t)NT * D * 2 +
+                           (size_t)kScoreWaves * kHistBins * sizeof(uint32_t);
+    static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+    static bool attr_set = false;  // benign race: every caller sets the same value
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)score_bf16_kernel<D, HT, NT, DB>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    score_bf16_kernel<D, HT, NT, DB><<<grid, 512, lds, s>>>(a);
+    return hipGetLastError();
+}
+
 template <int D, int HT>
 hipError_t launch_bf16_tile(const ScoreArgs &a, int32_t key_tile, dim3 grid, hipStream_t s)
 {
+    // 8 x 2048 x 4 B of histograms share LDS with the key tiles: 256-key
+    // tiles of 128 dims are single-buffered to stay within 160 KiB.
     switch (key_tile) {
-    case 64: score_bf16_kernel<D, HT, 64><<<grid, 512, 0, s>>>(a); break;
-    case 128: score_bf16_kernel<D, HT, 128><<<grid, 512, 0, s>>>(a); break;
-    case 256: score_bf16_kernel<D, HT, 256><<<grid, 512, 0, s>>>(a); break;
+    case 64: return launch_bf16_cfg<D, HT, 64, true>(a, grid, s);
+    case 128: return launch_bf16_cfg<D, HT, 128, true>(a, grid, s);
+    case 256: return launch_bf16_cfg<D, HT, 256, (D < 128)>(a, grid, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int D>
@@ -229,12 +416,12 @@ hipError_t launch_bf16_d(const ScoreArgs &a, int32_t key_tile, dim3 grid, hipStr
 }  // namespace
 
 hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t key_tile,
-                        int64_t ysplit, hipStream_t stream)
+                        hipStream_t stream)
 {
     if (a.rows <= 0) return hipSuccess;
     if (dtype == DT_BF16) {
         const int64_t nqb = (a.rows + kScoreWaves - 1) / kScoreWaves;
-        dim3 grid((unsigned)nqb, (unsigned)ysplit);
+        dim3 grid((unsigned)nqb);
         switch (D) {
         case 32: return launch_bf16_d<32>(a, key_tile, grid, stream);
         case 64: return launch_bf16_d<64>(a, key_tile, grid, stream);

@@ -60,7 +60,7 @@ def test_workspace_zero_without_usable_keys():
 
 def test_workspace_single_chunk_when_small():
     # 1024 rows, last row sees 256 keys: one chunk of 256 keys, no lists.
-    assert _ws(1024, 256, H=4, D=32, k=16) == 1024 * 256 * 4
+    assert _ws(1024, 256, H=4, D=32, k=16) == 1024 * 256 * 4 + 1024 * 16
 
 
 def test_workspace_tiny_budget_still_fits_one_block():

@@ -73,9 +73,10 @@ __device__ inline float relu_bits(float x)
 // running k-th key theta, and at the end of the chunk reduces it to the bin
 // b* that holds the k-th best of those keys (ChunkMeta).  The select kernel
 // then only has to look at keys in bins >= b*.
-template <int D, int HT, int NT, bool DB>
-__global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
+template <int D, int HT, int NT, bool DB, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
 {
+    constexpr int THREADS = WAVES * 64;
     constexpr int KSTEPS = D / 16;     // MFMA k-steps over the head dimension
     constexpr int HALF = KSTEPS / 2;   // k-steps per pipeline step
     constexpr int CH = D / 8;          // 16-byte chunks per key row
@@ -95,11 +96,11 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
     const int half = lane >> 5;   // which 8-dim k slice (A, B) / which 4-row group (C)
     const int col = lane & 31;    // key column (B, C) or head row (A)
 
-    const int64_t nqb = (a.rows + kScoreWaves - 1) / kScoreWaves;
+    const int64_t nqb = (a.rows + WAVES - 1) / WAVES;
     const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;
-    const int64_t rl = qb * kScoreWaves + wave;       // row within the batch
+    const int64_t rl = qb * WAVES + wave;       // row within the batch
     const bool active = rl < a.rows;
-    const int64_t last = min(qb * kScoreWaves + kScoreWaves - 1, a.rows - 1);
+    const int64_t last = min(qb * WAVES + WAVES - 1, a.rows - 1);
     const int64_t n_hi = n_usable(a.q_pos0 + a.row0 + last, a.T, a.m);
     const int64_t kb0 = a.c0;
     const int64_t kcap = a.c0 + a.clen;
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
         u_floor = (uint32_t)(th >> 32);
     }
 
-    for (int e = tid; e < kScoreWaves * kHistBins; e += 512) hist_all[e] = 0u;
+    for (int e = tid; e < WAVES * kHistBins; e += THREADS) hist_all[e] = 0u;
 
     // Resident A operand: q[row, ht*32 + col, ks*16 + half*8 .. +7], and the
     // head weights of the accumulator rows this lane holds.  Every load is
@@ -166,13 +167,13 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
     // outstanding global memory operations.)  Keys past the last usable one
     // read a clamped (valid, unused) key.
     constexpr int NCHUNK = NT * CH;                // 16-byte chunks per tile
-    constexpr int PER = (NCHUNK + 511) / 512;      // chunks per thread
+    constexpr int PER = (NCHUNK + THREADS - 1) / THREADS;      // chunks per thread
     u32x4 st[PER];
     auto gload = [&](int t) {
         const int64_t base = kb0 + (int64_t)t * NT;
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = min(p * 512 + tid, NCHUNK - 1);
+            const int c = min(p * THREADS + tid, NCHUNK - 1);
             const int key = c / CH;
             const int ch = c % CH;
             int64_t gk = base + key;
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
     auto lstore = [&](int buf) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int c = p * 512 + tid;
+            const int c = p * THREADS + tid;
             if (c < NCHUNK) {
                 const int key = c / CH;
                 const int ch = c % CH;
@@ -191,14 +192,18 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
             }
         }
     };
+    // Lane offsets of the B fragments inside a 32-key block: key col, chunk
+    // 2*ks + half, swizzled by col % CH (block starts are multiples of 32
+    // keys, so the swizzle does not depend on the block).
+    int boff[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+        boff[ks] = col * ROWB + (((2 * ks + half) ^ (col & (CH - 1))) << 4);
     // B fragments of half-step hs (k-steps hs*HALF .. +HALF-1) of block kb.
     auto load_b = [&](const unsigned char *tb, int kb, int hs, bf16x8 (&b)[HALF]) {
-        const int key = kb * 32 + col;
 #pragma unroll
-        for (int j = 0; j < HALF; ++j) {
-            const int ch = 2 * (hs * HALF + j) + half;
-            b[j] = *(const bf16x8 *)(tb + key * ROWB + ((ch ^ (key & (CH - 1))) << 4));
-        }
+        for (int j = 0; j < HALF; ++j)
+            b[j] = *(const bf16x8 *)(tb + kb * 32 * ROWB + boff[hs * HALF + j]);
     };
     auto mfma_half = [&](const bf16x8 (&b)[HALF], int hs, f32x16 (&acc)[HT]) {
 #pragma unroll
@@ -222,15 +227,15 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
     uint32_t *h = hist_all + wave * kHistBins;
 
     // Per-lane share of one block, over register half rh (8 of the 16
-    // accumulator rows of each 32-head block): ReLU and weighted sum.
-    auto partial = [&](const f32x16 (&acc)[HT], int rh, float &s0, float &s1) {
+    // accumulator rows of each 32-head block): ReLU and weighted sum, one
+    // FMA chain in a fixed order (rows of half 0 of every head block, then
+    // half 1).
+    auto partial = [&](const f32x16 (&acc)[HT], int rh, float &sum) {
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
-            for (int r = rh * 8; r < rh * 8 + 8; ++r) {
-                if (ht & 1) s1 = fmaf(wv[ht][r], relu_bits(acc[ht][r]), s1);
-                else s0 = fmaf(wv[ht][r], relu_bits(acc[ht][r]), s0);
-            }
+            for (int r = rh * 8; r < rh * 8 + 8; ++r)
+                sum = fmaf(wv[ht][r], relu_bits(acc[ht][r]), sum);
         }
     };
     // Finishes blocks 2p and 2p+1 (pe, po: each lane's share of them).  The
@@ -240,15 +245,36 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
     // the row's last key store into unused slots of the row (tiles never run
     // past the chunk, whose length is a multiple of NT) and add 0 to the
     // histogram.
-    auto finish2 = [&](float pe, float po, int rel0) {
+    auto finish2 = [&](float pe, float po, int rel0, bool real) {
         const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe), __float_as_uint(po),
                                                         false, false);
         const float sc = __uint_as_float(z[0]) + __uint_as_float(z[1]);
         const int rel = rel0 + lane;
-        const bool valid = rel < my_len;
+        const bool valid = real && rel < my_len;
         wsrow[rel] = sc;
         const uint32_t inc = (valid && (!filt || sc > f_floor)) ? 1u : 0u;
         atomicAdd(&h[orderable(sc) >> (32 - kHistBits)], inc);
+    };
+
+    // The last block of a tile is finished under the first block's MFMAs of
+    // the wave's next tile (or flushed when there is none): acc[1] and the
+    // pair state carry over the tile boundary.  On a wave's first tile the
+    // carried slot holds zeros and its finish counts nothing; its store goes
+    // to slots 0..63 of the row, which the tile's own first pair overwrites.
+    f32x16 acc[2][HT];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[i][ht] = f32x16{};
+    float pe_c = 0.0f;  // even-block share of the carried pair
+    int rel_c = 0;      // first key of the carried pair
+    bool pend = false;  // a carried pair is waiting
+    auto flush = [&]() {
+        float pacc = 0.0f;
+        partial(acc[1], 0, pacc);
+        partial(acc[1], 1, pacc);
+        finish2(pe_c, pacc, rel_c, true);
+        pend = false;
     };
 
     gload(0);
@@ -261,9 +287,9 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
         if (active && rel_t < my_len) {
             const unsigned char *tb = lds + (DB ? (t & 1) * TILEB : 0);
             bf16x8 bb[2][HALF];
-            f32x16 acc[2][HT];
             float pacc = 0.0f;  // share of the block being finished
             float pe = 0.0f;    // share of the even block of the current pair
+            const bool real_c = pend;
             load_b(tb, 0, 0, bb[0]);
 #pragma unroll
             for (int step = 0; step < 2 * NB; ++step) {
@@ -273,26 +299,21 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
                 // Keep the prefetch here, one step ahead of its use.
                 __builtin_amdgcn_sched_barrier(0);
                 mfma_half(bb[step & 1], hs, acc[kb & 1]);
-                if (kb > 0) {  // half hs of block kb-1's epilogue, under block kb's MFMAs
-                    float s0 = 0.0f, s1 = 0.0f;
-                    partial(acc[(kb - 1) & 1], hs, s0, s1);
-                    pacc = hs == 0 ? s0 + s1 : pacc + (s0 + s1);
-                    if (hs == 1) {
-                        if (((kb - 1) & 1) == 0) pe = pacc;
-                        else finish2(pe, pacc, rel_t + (kb - 2) * 32);
-                    }
+                // Half hs of the previous block's epilogue, under these MFMAs
+                // (for kb == 0 the previous block is the carried one, acc[1]).
+                if (hs == 0) pacc = 0.0f;
+                partial(acc[(kb + 1) & 1], hs, pacc);
+                if (hs == 1) {
+                    if (kb == 0) finish2(pe_c, pacc, rel_c, real_c);
+                    else if (((kb - 1) & 1) == 0) pe = pacc;
+                    else finish2(pe, pacc, rel_t + (kb - 2) * 32, true);
                 }
             }
-            {  // last block of the tile
-                float s0 = 0.0f, s1 = 0.0f;
-                partial(acc[(NB - 1) & 1], 0, s0, s1);
-                pacc = s0 + s1;
-                s0 = 0.0f;
-                s1 = 0.0f;
-                partial(acc[(NB - 1) & 1], 1, s0, s1);
-                pacc = pacc + (s0 + s1);
-                finish2(pe, pacc, rel_t + (NB - 2) * 32);
-            }
+            pe_c = pe;  // the tile's last pair (blocks NB-2, NB-1) is carried
+            rel_c = rel_t + (NB - 2) * 32;
+            pend = true;
+        } else if (pend) {
+            flush();
         }
         if (more) {
             if constexpr (!DB) __syncthreads();  // single buffer: all reads done
@@ -300,6 +321,7 @@ __global__ __launch_bounds__(512) void score_bf16_kernel(ScoreArgs a)
         }
         __syncthreads();
     }
+    if (pend) flush();
 
     // Chunk summary: locate the bin that holds the k-th best counted key.
     if (active && a.meta) {
@@ -376,41 +398,43 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a)
     a.ws[rl * a.clen + (gk - a.c0)] = s;
 }
 
-template <int D, int HT, int NT, bool DB>
-hipError_t launch_bf16_cfg(const ScoreArgs &a, dim3 grid, hipStream_t s)
+template <int D, int HT, int NT, bool DB, int WAVES>
+hipError_t launch_bf16_cfg(const ScoreArgs &a, hipStream_t s)
 {
     constexpr size_t lds = (DB ? 2 : 1) * (size_t)NT * D * 2 +
-                           (size_t)kScoreWaves * kHistBins * sizeof(uint32_t);
+                           (size_t)WAVES * kHistBins * sizeof(uint32_t);
     static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 workgroup");
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)score_bf16_kernel<D, HT, NT, DB>,
+        hipError_t e = hipFuncSetAttribute((const void *)score_bf16_kernel<D, HT, NT, DB, WAVES>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    score_bf16_kernel<D, HT, NT, DB><<<grid, 512, lds, s>>>(a);
+    const dim3 grid((unsigned)((a.rows + WAVES - 1) / WAVES));
+    score_bf16_kernel<D, HT, NT, DB, WAVES><<<grid, WAVES * 64, lds, s>>>(a);
     return hipGetLastError();
 }
 
 template <int D, int HT>
-hipError_t launch_bf16_tile(const ScoreArgs &a, int32_t key_tile, dim3 grid, hipStream_t s)
+hipError_t launch_bf16_tile(const ScoreArgs &a, int32_t key_tile, hipStream_t s)
 {
-    // 8 x 2048 x 4 B of histograms share LDS with the key tiles: 256-key
-    // tiles of 128 dims are single-buffered to stay within 160 KiB.
+    // 8-row workgroups, one per CU; 256-key tiles of 128 dims are
+    // single-buffered to stay within 160 KiB next to the 64 KiB of
+    // histograms.  (Two 4-row workgroups per CU were measured slower.)
     switch (key_tile) {
-    case 64: return launch_bf16_cfg<D, HT, 64, true>(a, grid, s);
-    case 128: return launch_bf16_cfg<D, HT, 128, true>(a, grid, s);
-    case 256: return launch_bf16_cfg<D, HT, 256, (D < 128)>(a, grid, s);
+    case 64: return launch_bf16_cfg<D, HT, 64, true, 8>(a, s);
+    case 128: return launch_bf16_cfg<D, HT, 128, true, 8>(a, s);
+    case 256: return launch_bf16_cfg<D, HT, 256, (D < 128), 8>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int D>
-hipError_t launch_bf16_d(const ScoreArgs &a, int32_t key_tile, dim3 grid, hipStream_t s)
+hipError_t launch_bf16_d(const ScoreArgs &a, int32_t key_tile, hipStream_t s)
 {
-    if (a.H <= 32) return launch_bf16_tile<D, 1>(a, key_tile, grid, s);
-    return launch_bf16_tile<D, 2>(a, key_tile, grid, s);
+    if (a.H <= 32) return launch_bf16_tile<D, 1>(a, key_tile, s);
+    return launch_bf16_tile<D, 2>(a, key_tile, s);
 }
 
 }  // namespace
@@ -420,12 +444,10 @@ hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t ke
 {
     if (a.rows <= 0) return hipSuccess;
     if (dtype == DT_BF16) {
-        const int64_t nqb = (a.rows + kScoreWaves - 1) / kScoreWaves;
-        dim3 grid((unsigned)nqb);
         switch (D) {
-        case 32: return launch_bf16_d<32>(a, key_tile, grid, stream);
-        case 64: return launch_bf16_d<64>(a, key_tile, grid, stream);
-        case 128: return launch_bf16_d<128>(a, key_tile, grid, stream);
+        case 32: return launch_bf16_d<32>(a, key_tile, stream);
+        case 64: return launch_bf16_d<64>(a, key_tile, stream);
+        case 128: return launch_bf16_d<128>(a, key_tile, stream);
         default: return hipErrorInvalidValue;
         }
     }

@@ -33,6 +33,7 @@ from streaming_indexer_top_amd import inputs  # noqa: E402
 
 METRIC = "scored q-k pairs/s at S=65536 V4-Flash dims; MFMA util %; peak HBM GB"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_BUSY_PEAK = MFMA_BF16_PEAK_TFLOPS
 HBM_PEAK_GBS = 8000.0
 
 
@@ -90,6 +91,53 @@ def cpu_baseline(q, w, kc, m, k, S, T, target_s, max_rows, seed):
     }, rows, res
 
 
+def run_sweep(args, q, w, kc, c, dev, base_alloc):
+    """Chunk-size x key-tile sweep: time per call, throughput, peak HBM, and a
+    bit-identity check of every setting's outputs against the first one's."""
+    S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    P = pair_count(S, T, m)
+    idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+    score = torch.empty((S, k), dtype=torch.float32, device=dev)
+    ref = None
+    for chunk in [int(x) for x in args.sweep_chunks.split(",")]:
+        for tile in [int(x) for x in args.sweep_tiles.split(",")]:
+            ws_bytes = csa.workspace_size(S, T, H, D, m, k, chunk_keys=chunk, key_tile=tile,
+                                          workspace_budget=args.budget)
+            torch.cuda.reset_peak_memory_stats(dev)
+            workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+            kw = dict(chunk_keys=chunk, key_tile=tile, workspace_budget=args.budget,
+                      workspace=workspace, out=(idx, score))
+            for _ in range(args.warmup):
+                csa.topk(q, w, kc, m, k, **kw)
+            torch.cuda.synchronize()
+            csa.profile_collect()
+            csa.profile_enable(True)
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                csa.topk(q, w, kc, m, k, **kw)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            csa.profile_enable(False)
+            prof = csa.profile_collect()
+            ms = (t1 - t0) * 1e3 / args.steps
+            if ref is None:
+                ref = (idx.clone(), score.clone())
+                same = True
+            else:
+                same = bool(torch.equal(ref[0], idx)) and bool(
+                    torch.equal(ref[1].view(torch.int32), score.view(torch.int32)))
+            peak = torch.cuda.max_memory_allocated(dev) - base_alloc
+            print(json.dumps({
+                "workload": args.workload, "S": S, "T": T, "chunk_keys": chunk, "key_tile": tile,
+                "ms_per_call": ms, "pairs_per_s": P / (ms * 1e-3),
+                "mfma_util_pct": 100.0 * P * 2 * H * D / (ms * 1e-3) / (MFMA_BUSY_PEAK * 1e12),
+                "score_ms": prof["score"][0] / args.steps, "select_ms": prof["select"][0] / args.steps,
+                "score_launches": prof["score"][1] / args.steps,
+                "workspace_bytes": ws_bytes, "peak_hbm_gib": peak / 2 ** 30,
+                "bit_identical_to_first": same}), flush=True)
+            del workspace
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +150,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-max-rows", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every chunk x key-tile setting (default grid: chunk 4096..65536, "
+                         "tile 64/128/256), one JSON line each, checking that all settings give "
+                         "bit-identical outputs")
+    ap.add_argument("--sweep-chunks", default="4096,8192,16384,32768,65536")
+    ap.add_argument("--sweep-tiles", default="64,128,256")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device copy run once before timing, as a known "
                          "reference for HBM traffic counters")
@@ -125,6 +179,10 @@ def main():
     torch.cuda.synchronize()
     gen_peak = torch.cuda.max_memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
+
+    if args.sweep:
+        run_sweep(args, q, w, kc, c, dev, base_alloc)
+        return
 
     ws_bytes = csa.workspace_size(S, T, H, D, m, k, chunk_keys=args.chunk, key_tile=args.tile,
                                   workspace_budget=args.budget)

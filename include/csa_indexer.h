@@ -90,7 +90,7 @@ typedef struct csa_opts {
     int32_t key_tile;
     int32_t reserved0; /* must be 0 */
     /* Upper bound, in bytes, on the workspace that
-     * csa_indexer_topk_workspace_size plans for; 0 means 1 GiB.  A smaller
+     * csa_indexer_topk_workspace_size plans for; 0 means 2 GiB.  A smaller
      * workspace only makes the library process fewer query rows per pass. */
     int64_t workspace_budget;
     int64_t reserved[4]; /* must be 0 */

@@ -22,9 +22,9 @@
 
 namespace {
 
-constexpr int64_t kDefaultBudget = int64_t(1) << 30;
-constexpr int64_t kDefaultChunkCap = 32768;  // single chunk up to this many keys
-constexpr int64_t kDefaultChunk = 16384;
+constexpr int64_t kDefaultBudget = int64_t(2) << 30;
+constexpr int64_t kDefaultChunkCap = 65536;  // single chunk up to this many keys
+constexpr int64_t kDefaultChunk = 65536;
 constexpr int32_t kDefaultTile = 128;
 constexpr size_t kAlign = 256;
 

@@ -429,17 +429,75 @@ __device__ int collect_all(uint64_t *cand, const RowCtx &r, SelectShared &sh, in
 // histogram summary: keys above bin b* are all in, keys in b* compete for the
 // remaining places by an exact radix select on their remaining bits.  The
 // bin edges are turned into fp32 thresholds (orderable() is monotone), so a
-// key is classified by two float compares.
+// key is classified by two float compares.  When bin b* holds more keys than
+// the boundary buffer, one extra pass histograms the next 8 bits of the keys
+// in b* and narrows the boundary to one sub-bin.  Returns -1 if even the
+// sub-bin does not fit (massively tied scores); the caller falls back.
 __device__ int collect_by_bin(uint64_t *cand, const RowCtx &r, const ChunkMeta &mt, int k,
                               SelectShared &sh, int tid)
 {
-    uint64_t *bnd = cand + k;  // boundary-bin entries
+    uint64_t *bnd = cand + k;  // boundary entries
     const bool filt = r.filt;
     const float f_floor = score_of_orderable(r.u_floor);
-    // Smallest scores of bins b*+1 and b* (bin 0 starts at -inf).
-    const float f_sure = score_of_orderable((mt.bin + 1u) << (32 - kHistBits));
-    const float f_edge = mt.bin == 0u ? -__builtin_inff()
-                                      : score_of_orderable(mt.bin << (32 - kHistBits));
+    constexpr int BIN_SHIFT = 32 - kHistBits;  // orderable bits below the bin
+    uint32_t lo_u = mt.bin << BIN_SHIFT;        // boundary: orderable in [lo_u, hi_u)
+    uint32_t hi_u = (mt.bin + 1u) << BIN_SHIFT;
+    int need = k - (int)mt.above;
+    int first_shift = 64 - kHistBits - 8;
+    if (mt.in_bin > (uint32_t)kSelectPiece) {
+        // Histogram of orderable bits [BIN_SHIFT-8, BIN_SHIFT) inside bin b*.
+        sh.hist[tid] = 0u;
+        __syncthreads();
+        const float f_lo = mt.bin == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
+        const float f_hi = score_of_orderable(hi_u);
+        const int lane = tid & 63;
+        for (int64_t e0 = 0; e0 < r.len; e0 += NT) {
+            const int64_t e = e0 + tid;
+            bool in = false;
+            uint32_t d = 0;
+            if (e < r.len) {
+                const float x = r.src[e];
+                in = (!filt || x > f_floor) && x >= f_lo && !(x >= f_hi);
+                d = (orderable(x) >> (BIN_SHIFT - 8)) & 255u;
+            }
+            hist_add(sh.hist, in, d, lane);
+        }
+        __syncthreads();
+        if (tid < 64) {
+            uint32_t h4[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) h4[b] = sh.hist[4 * tid + b];
+            const uint32_t local = h4[0] + h4[1] + h4[2] + h4[3];
+            uint32_t incl = local;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t y = __shfl_down(incl, off);
+                if (tid + off < 64) incl += y;
+            }
+            uint32_t above = incl - local;
+#pragma unroll
+            for (int b = 3; b >= 0; --b) {
+                if (above < (uint32_t)need && (uint32_t)need <= above + h4[b]) {
+                    sh.digit = (uint32_t)(4 * tid + b);
+                    sh.above = above;
+                    sh.bin = h4[b];
+                }
+                above += h4[b];
+            }
+        }
+        __syncthreads();
+        const uint32_t dsub = sh.digit;
+        need -= (int)sh.above;
+        const uint32_t sub_cnt = sh.bin;
+        __syncthreads();
+        if (sub_cnt > (uint32_t)kSelectPiece) return -1;
+        lo_u |= dsub << (BIN_SHIFT - 8);
+        hi_u = lo_u + (1u << (BIN_SHIFT - 8));
+        first_shift -= 8;
+    }
+    // Boundary edges as fp32 thresholds (bin 0 starts at -inf).
+    const float f_sure = score_of_orderable(hi_u);
+    const float f_edge = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
     int above, in_bin;
     collect2(
         r,
@@ -448,8 +506,8 @@ __device__ int collect_by_bin(uint64_t *cand, const RowCtx &r, const ChunkMeta &
             return x >= f_sure ? 1u : (x >= f_edge ? 2u : 0u);
         },
         cand, bnd, above, in_bin, sh, tid);
-    const int need = k - above;
-    if (in_bin > need) radix_select(bnd, in_bin, need, sh, tid, 64 - kHistBits - 8);
+    need = k - above;
+    if (in_bin > need) radix_select(bnd, in_bin, need, sh, tid, first_shift);
     for (int e = tid; e < need; e += NT) cand[above + e] = bnd[e];
     __syncthreads();
     return k;
@@ -536,10 +594,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
             const ChunkMeta mt = a.meta[rl];
             if (mt.total <= (uint32_t)k) {
                 cnt_q = collect_all(cand, r, sh, tid);
-            } else if (mt.in_bin <= (uint32_t)kSelectPiece) {
-                cnt_q = collect_by_bin(cand, r, mt, k, sh, tid);
             } else {
-                cnt_q = collect_pieces(cand, r, k, sh, tid);
+                cnt_q = collect_by_bin(cand, r, mt, k, sh, tid);
+                if (cnt_q < 0) cnt_q = collect_pieces(cand, r, k, sh, tid);
             }
         } else {
             cnt_q = collect_pieces(cand, r, k, sh, tid);

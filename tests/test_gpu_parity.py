@@ -111,6 +111,26 @@ def test_empty_query_set():
     assert g_idx.shape == (0, 3) and g_sc.shape == (0, 3)
 
 
+def test_crowded_threshold_bin_is_refined():
+    """Every score lies in [1.0, 1.25), one bin of the score kernel's
+    histogram, so the select kernel must split that bin by its next bits
+    (more keys than its boundary buffer holds) and still return the exact
+    top-k by the tolerance rules."""
+    S, T, H, D, m, k, q_pos0 = 16, 8192, 1, 128, 1, 64, 10000
+    g = torch.Generator().manual_seed(12)
+    q = torch.full((S, H, D), 1.0 / 128, dtype=torch.bfloat16)
+    w = torch.ones((S, H), dtype=torch.bfloat16)
+    kc = (1.0 + 0.2 * torch.rand((T, D), generator=g)).to(torch.bfloat16)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    assert np.all((g_sc >= 1.0) & (g_sc < 1.25))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    fails, stats = checks.check_float(g_idx, g_sc, o_idx, o_sc, q.float().numpy(),
+                                      w.float().numpy(), kc.float().numpy(),
+                                      np.arange(S) + q_pos0, T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
 def test_signed_zero_scores_are_positive():
     # Every head dot product is <= 0 and the weights are negative: every score
     # is zero and must come out as +0, with ties broken by index.

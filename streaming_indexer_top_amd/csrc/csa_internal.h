@@ -93,7 +93,7 @@ hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t ke
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 
 // Keys of one chunk piece that the select kernel stages in LDS at a time.
-constexpr int kSelectPiece = 4096;
+constexpr int kSelectPiece = 2048;
 constexpr int kSelectThreads = 256;
 constexpr int kScoreWaves = 8;  // query rows per score workgroup (one per wave)
 

@@ -5,19 +5,26 @@
 // its central component: keys are split into chunks, each query keeps its top
 // keys per chunk and the partial lists are merged, so the full score tensor
 // never exists.  This kernel is that step for one chunk: one workgroup per
-// query row reads the row's chunk scores from the workspace, keeps only those
-// that can still enter the row's running best-k list, and whenever the
-// candidates exceed k selects the best k exactly.  After the last chunk it
-// sorts the list and writes the row's outputs.
+// query row reads the row's chunk scores from the workspace once, keeps only
+// those that can still enter the row's best k, sorts them, merges them with
+// the row's running list and, after the last chunk, writes the row's outputs.
 //
 // Exactness: every (score, key) pair is mapped to a 64-bit orderable key
 //     key = (orderable(score) << 32) | (0xFFFFFFFF - j)
 // where orderable() is the monotone map of fp32 onto uint32 after -0 -> +0.
 // A larger key means a better entry under (score desc, index asc), and keys
 // are unique because j is, so the best k is a well-defined set whatever the
-// chunking: top-k(A u B) = top-k(top-k(A) u top-k(B)).  Selection is a
-// most-significant-digit radix select on these keys (8-bit digits, LDS
-// histograms), so the outputs are bit-identical for every chunk size.
+// chunking: top-k(A u B) = top-k(top-k(A) u top-k(B)).  Every decision below
+// (which keys are kept, their order) is taken on these keys, so the outputs
+// are bit-identical for every chunk size.
+//
+// Common path (bf16 scores with the score kernel's histogram summary): the
+// summary names the bin b* (top 11 orderable bits) holding the chunk's k-th
+// best key.  One streaming pass sorts each chunk key into "above b*" (all
+// kept, fewer than k), "in b*" (the boundary) or dropped, and appends the kept
+// ones to two LDS regions.  One bucket sort over both regions orders them;
+// the first k are the chunk's best k.  The workgroup needs about 39 KB of LDS,
+// so four rows share a CU.
 #include "csa_internal.h"
 
 namespace csa {
@@ -25,7 +32,14 @@ namespace {
 
 constexpr int NT = kSelectThreads;
 constexpr int NWAVES = NT / 64;
-constexpr int PER_MAX = (2048 + kSelectPiece + NT - 1) / NT;  // entries per thread, k <= 2048
+constexpr int kCapA = 2048;           // keys above the boundary bin (< k <= 2048)
+constexpr int kCapB = 2048;           // keys in the boundary bin
+constexpr int kCand = kCapA + kCapB;  // 64-bit key slots in LDS
+constexpr int kBuckets = 1536;        // bucket sort: one 32-bit word per bucket
+constexpr int kSortMaxBucket = 64;    // larger buckets: bitonic sort instead
+constexpr int PER_MAX = kCand / NT;   // keys per thread in the sort and radix select
+static_assert(kSelectPiece + 2048 <= kCand, "fallback pieces must fit beside k keys");
+static_assert(kBuckets % NT == 0 && kBuckets >= 256, "bucket words double as a 256-bin histogram");
 
 __device__ inline float key_score(uint64_t key)
 {
@@ -55,8 +69,51 @@ __device__ inline uint32_t lanes_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Adds this lane's digit to the histogram.  Lanes of a wave that share a
-// digit are counted together (a few rounds of "take the first pending lane's
+// Inclusive prefix sum over the 64 lanes of a wave (DPP: shifts within rows
+// of 16 lanes, then the row totals broadcast to the rows above).
+__device__ inline uint32_t wave_incl_sum(uint32_t x)
+{
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false); // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false); // row_bcast:31
+    return x;
+}
+
+__device__ inline uint32_t wave_min_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, off);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+__device__ inline uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)v, off);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+__device__ inline uint64_t wave_min_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(v, off);
+        v = o < v ? o : v;
+    }
+    return v;
+}
+
+// Adds this lane's digit to a histogram.  Lanes of a wave that share a digit
+// are counted together (a few rounds of "take the first pending lane's
 // digit, ballot the lanes with the same digit, one atomic for all of them"),
 // because score digits cluster and same-address LDS atomics serialise.
 __device__ inline void hist_add(uint32_t *hist, bool in, uint32_t d, int lane)
@@ -76,22 +133,13 @@ __device__ inline void hist_add(uint32_t *hist, bool in, uint32_t d, int lane)
 }
 
 struct SelectShared {
-    uint32_t hist[256];
     uint64_t wmin[NWAVES];
     uint32_t wsum[NWAVES];
-    uint32_t count, count2;
+    uint32_t wred[NWAVES][4];
+    uint32_t nA, nB;
+    uint32_t count;
     uint32_t digit, above, bin;
 };
-
-__device__ inline uint64_t wave_min_u64(uint64_t v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint64_t o = __shfl_xor(v, off);
-        v = o < v ? o : v;
-    }
-    return v;
-}
 
 // Minimum of cand[0..cnt) over the block (cnt > 0).
 __device__ uint64_t block_min(const uint64_t *cand, int cnt, SelectShared &sh, int tid)
@@ -111,14 +159,8 @@ __device__ uint64_t block_min(const uint64_t *cand, int cnt, SelectShared &sh, i
 // Exclusive prefix sum of v over the block (thread order), and the total.
 __device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t &total, SelectShared &sh, int tid)
 {
-    const int lane = tid & 63;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) sh.wsum[tid >> 6] = x;
+    const uint32_t x = wave_incl_sum(v);
+    if ((tid & 63) == 63) sh.wsum[tid >> 6] = x;
     __syncthreads();
     uint32_t before = 0;
     total = 0;
@@ -132,18 +174,49 @@ __device__ uint32_t block_exclusive_sum(uint32_t v, uint32_t &total, SelectShare
     return before + x - v;
 }
 
-// Keeps the k largest of cand[0..cnt) (cnt > k) in cand[0..k), any order.
-// All entries must agree on the key bits above `first_shift + 8`; digits are
-// 8 bits wide from there down (the last digit is clamped at bit 0).
-__device__ void radix_select(uint64_t *cand, int cnt, int k, SelectShared &sh, int tid,
-                             int first_shift = 56)
+// Of the 256 bins of hist, finds the one holding the need-th largest entry
+// (bins in descending order): sh.digit = that bin, sh.above = entries in
+// higher bins, sh.bin = entries in it.  Wave 0 works; the caller syncs.
+__device__ inline void find_digit(const uint32_t *hist, uint32_t need, SelectShared &sh, int tid)
+{
+    if (tid >= 64) return;
+    const int lane = tid;
+    // Lane l owns bins 4l..4l+3; above(l) = entries in bins of higher lanes.
+    uint32_t h[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) h[b] = hist[4 * lane + b];
+    const uint32_t local = h[0] + h[1] + h[2] + h[3];
+    uint32_t incl = local;  // sum over lanes >= this lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(incl, off);
+        if (lane + off < 64) incl += y;
+    }
+    uint32_t above = incl - local;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+        if (above < need && need <= above + h[b]) {
+            sh.digit = (uint32_t)(4 * lane + b);
+            sh.above = above;
+            sh.bin = h[b];
+        }
+        above += h[b];
+    }
+}
+
+// Keeps the k largest of cand[0..cnt) (k < cnt <= kCand) in cand[0..k), any
+// order.  All entries must agree on the key bits above `first_shift + 8`;
+// digits are 8 bits wide from there down (the last one clamped at bit 0).
+// hist has 256 words.
+__device__ void radix_select(uint64_t *cand, int cnt, int k, uint32_t *hist, SelectShared &sh,
+                             int tid, int first_shift = 56)
 {
     const int lane = tid & 63;
     uint32_t need = (uint32_t)k;
     uint64_t prefix = 0, mask = 0;
     for (int shift = first_shift;; shift -= 8) {
         if (shift < 0) shift = 0;
-        sh.hist[tid] = 0u;  // NT == 256 bins
+        hist[tid] = 0u;  // NT == 256 bins
         __syncthreads();
         const int rounds = (cnt + NT - 1) / NT;
         for (int rd = 0; rd < rounds; ++rd) {
@@ -154,39 +227,18 @@ __device__ void radix_select(uint64_t *cand, int cnt, int k, SelectShared &sh, i
                 key = cand[e];
                 in = (key & mask) == prefix;
             }
-            hist_add(sh.hist, in, (uint32_t)(key >> shift) & 255u, lane);
+            hist_add(hist, in, (uint32_t)(key >> shift) & 255u, lane);
         }
         __syncthreads();
-        if (tid < 64) {
-            // Lane l owns bins 4l..4l+3.  above(l) = entries in bins of
-            // higher lanes; scan runs from lane 63 downwards.
-            uint32_t h[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) h[b] = sh.hist[4 * lane + b];
-            const uint32_t local = h[0] + h[1] + h[2] + h[3];
-            uint32_t incl = local;  // sum over lanes >= this lane
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = __shfl_down(incl, off);
-                if (lane + off < 64) incl += y;
-            }
-            uint32_t above = incl - local;
-#pragma unroll
-            for (int b = 3; b >= 0; --b) {
-                if (above < need && need <= above + h[b]) {
-                    sh.digit = (uint32_t)(4 * lane + b);
-                    sh.above = above;
-                    sh.bin = h[b];
-                }
-                above += h[b];
-            }
-        }
+        find_digit(hist, need, sh, tid);
         __syncthreads();
         const uint32_t d = sh.digit;
         need -= sh.above;
         prefix |= (uint64_t)d << shift;
         mask |= 255ull << shift;
-        if (sh.bin == need || shift == 0) break;  // the whole bin is taken: done
+        const bool done = sh.bin == need || shift == 0;  // the whole bin is taken
+        __syncthreads();
+        if (done) break;
     }
     // Entries whose masked key is >= prefix are exactly the k best.
     uint64_t v[PER_MAX];
@@ -207,8 +259,9 @@ __device__ void radix_select(uint64_t *cand, int cnt, int k, SelectShared &sh, i
     __syncthreads();
 }
 
-// Sorts cand[0..n) descending (the buffer must hold the next power of two).
-__device__ void bitonic_desc(uint64_t *cand, int n, SelectShared &sh, int tid)
+// Sorts cand[0..n) descending; n <= kCand, and the buffer holds the next
+// power of two.  Used for degenerate inputs (huge runs of equal scores).
+__device__ void bitonic_desc(uint64_t *cand, int n, int tid)
 {
     int p2 = 2;
     while (p2 < n) p2 <<= 1;
@@ -231,152 +284,194 @@ __device__ void bitonic_desc(uint64_t *cand, int n, SelectShared &sh, int tid)
     }
 }
 
-// Sorts cand[0..n) descending through a bucket pass.  Keys are binned by
-// their score part into kSortBins buckets spread evenly over the row's
-// [min, max] score range (monotone, so bucket order is key order), scattered
-// into bucket order in tmp, and every key finds its place inside its bucket
-// by counting the larger keys there.  Buckets are small for spread-out
-// scores; if any bucket holds more than kSortMaxBucket keys (many equal or
-// clustered scores) the bitonic sort takes over.  `bins` has 2*kSortBins
-// words, `tmp` n entries (not overlapping cand).  Returns nothing; cand ends
-// up sorted either way.
-constexpr int kSortBins = 2048;
-constexpr int kSortMaxBucket = 64;
-
-__device__ void bucket_sort_desc(uint64_t *cand, uint64_t *tmp, int n, uint32_t *bins,
-                                 SelectShared &sh, int tid)
+// Sorts the nA keys at cand[0..nA) and the nB keys at cand[kCapA..kCapA+nB)
+// together, descending, into cand[0..nA+nB).  Every A key must be larger
+// than every B key (A = above the boundary, B = in it; either may be empty).
+//
+// Bucket sort with the keys held in registers: each region's score range
+// [min, max] is cut into buckets of equal width in score value (B gets a
+// share of the kBuckets buckets proportional to its size, A the rest), which
+// is monotone, so bucket order is key order.  One LDS atomic per key counts
+// its bucket and gives its slot there; a prefix sum over the buckets (from the
+// top) gives each bucket's first position; keys are scattered into bucket
+// order, and each then finds its place inside its bucket by counting the
+// larger keys there.  If a bucket holds more than kSortMaxBucket keys (many
+// equal or clustered scores) a bitonic sort of the whole buffer takes over.
+// bk: kBuckets words.
+__device__ void sort_keys(uint64_t *cand, int nA, int nB, uint32_t *bk, SelectShared &sh,
+                          int tid)
 {
     const int lane = tid & 63;
-    uint32_t *cnt = bins;               // bucket sizes, then insertion cursors
-    uint32_t *off = bins + kSortBins;   // first slot of each bucket (descending order)
-    // Score range of the keys (orderable, then as fp32 values).
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int e = tid; e < n; e += NT) {
-        const uint32_t u = (uint32_t)(cand[e] >> 32);
-        lo = u < lo ? u : lo;
-        hi = u > hi ? u : hi;
+    const int wave = tid >> 6;
+    constexpr int PT = PER_MAX;  // slots 0..PT/2-1 from A's region, the rest from B's
+    constexpr int PH = PT / 2;
+    uint64_t key[PT];
+    uint32_t loA = 0xFFFFFFFFu, hiA = 0u, loB = 0xFFFFFFFFu, hiB = 0u;
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int e = (i % PH) * NT + tid;
+        const bool inA = i < PH;
+        const bool v = e < (inA ? nA : nB);
+        key[i] = v ? cand[(inA ? 0 : kCapA) + e] : 0ull;
+        const uint32_t u = (uint32_t)(key[i] >> 32);
+        if (v && inA) {
+            loA = u < loA ? u : loA;
+            hiA = u > hiA ? u : hiA;
+        }
+        if (v && !inA) {
+            loB = u < loB ? u : loB;
+            hiB = u > hiB ? u : hiB;
+        }
     }
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t a = (uint32_t)__shfl_xor((int)lo, o), b = (uint32_t)__shfl_xor((int)hi, o);
-        lo = a < lo ? a : lo;
-        hi = b > hi ? b : hi;
-    }
-    for (int e = tid; e < kSortBins; e += NT) cnt[e] = 0u;
+    for (int e = tid; e < kBuckets; e += NT) bk[e] = 0u;
+    loA = wave_min_u32(loA);
+    hiA = wave_max_u32(hiA);
+    loB = wave_min_u32(loB);
+    hiB = wave_max_u32(hiB);
     if (lane == 0) {
-        sh.wsum[tid >> 6] = lo;
-        sh.wmin[tid >> 6] = hi;
+        sh.wred[wave][0] = loA;
+        sh.wred[wave][1] = hiA;
+        sh.wred[wave][2] = loB;
+        sh.wred[wave][3] = hiB;
     }
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < NWAVES; ++w) {
-        lo = sh.wsum[w] < lo ? sh.wsum[w] : lo;
-        hi = (uint32_t)sh.wmin[w] > hi ? (uint32_t)sh.wmin[w] : hi;
+        loA = sh.wred[w][0] < loA ? sh.wred[w][0] : loA;
+        hiA = sh.wred[w][1] > hiA ? sh.wred[w][1] : hiA;
+        loB = sh.wred[w][2] < loB ? sh.wred[w][2] : loB;
+        hiB = sh.wred[w][3] > hiB ? sh.wred[w][3] : hiB;
     }
-    // Buckets evenly spaced in score value: b = floor((s - lo) * scale), a
-    // monotone function of s, clamped to the bucket range.
-    const float flo = score_of_orderable(lo), fhi = score_of_orderable(hi);
-    const float scale = fhi > flo ? (float)(kSortBins - 1) / (fhi - flo) : 0.0f;
-    auto bucket = [&](uint64_t key) -> uint32_t {
-        const float x = (score_of_orderable((uint32_t)(key >> 32)) - flo) * scale;
-        const int b = (int)x;
-        return (uint32_t)(b < 0 ? 0 : (b > kSortBins - 1 ? kSortBins - 1 : b));
+    const int n = nA + nB;
+    int nbB = 0;
+    if (nB > 0) {
+        nbB = nA == 0 ? kBuckets : (int)((int64_t)kBuckets * nB / n);
+        nbB = nbB < 1 ? 1 : (nbB > kBuckets - 1 && nA > 0 ? kBuckets - 1 : nbB);
+    }
+    const int nbA = kBuckets - nbB;
+    const float fAlo = score_of_orderable(loA), fAhi = score_of_orderable(hiA);
+    const float fBlo = score_of_orderable(loB), fBhi = score_of_orderable(hiB);
+    const float scA = fAhi > fAlo ? (float)nbA / (fAhi - fAlo) : 0.0f;
+    const float scB = fBhi > fBlo ? (float)nbB / (fBhi - fBlo) : 0.0f;
+    // Bucket of a key: monotone in its score (clamps also catch inf/NaN).
+    auto bucket = [&](uint64_t kk, bool inA) -> uint32_t {
+        const float x = score_of_orderable((uint32_t)(kk >> 32));
+        float t = inA ? (x - fAlo) * scA : (x - fBlo) * scB;
+        t = fminf(fmaxf(t, 0.0f), (float)((inA ? nbA : nbB) - 1));
+        return (uint32_t)(int)t + (inA ? (uint32_t)nbB : 0u);
     };
-    // Histogram of the buckets.
-    for (int e0 = 0; e0 < n; e0 += NT) {
-        const int e = e0 + tid;
-        uint32_t b = 0;
-        if (e < n) b = bucket(cand[e]);
-        hist_add(cnt, e < n, b, lane);
+    uint32_t bkt[PT], slot[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int e = (i % PH) * NT + tid;
+        const bool inA = i < PH;
+        bkt[i] = 0u;
+        slot[i] = 0u;
+        if (e < (inA ? nA : nB)) {
+            bkt[i] = bucket(key[i], inA);
+            slot[i] = atomicAdd(&bk[bkt[i]], 1u);
+        }
     }
     __syncthreads();
-    // off[b] = keys in buckets above b; largest bucket.
-    constexpr int PB = kSortBins / NT;
+    // First position of every bucket, counted from the top bucket down;
+    // thread t owns buckets kBuckets-1-(t*PB .. t*PB+PB-1).  The words become
+    // (first position << 16) | size.
+    constexpr int PB = kBuckets / NT;
     uint32_t c[PB];
     uint32_t mine = 0, big = 0;
 #pragma unroll
-    for (int i = 0; i < PB; ++i) {
-        c[i] = cnt[kSortBins - 1 - (tid * PB + i)];  // thread order = descending buckets
-        mine += c[i];
-        big = c[i] > big ? c[i] : big;
+    for (int j = 0; j < PB; ++j) {
+        c[j] = bk[kBuckets - 1 - (tid * PB + j)];
+        mine += c[j];
+        big = c[j] > big ? c[j] : big;
     }
+    big = wave_max_u32(big);
+    if (lane == 0) sh.wred[wave][0] = big;
     uint32_t total;
-    uint32_t run = block_exclusive_sum(mine, total, sh, tid);
+    uint32_t run = block_exclusive_sum(mine, total, sh, tid);  // barriers inside
 #pragma unroll
-    for (int i = 0; i < PB; ++i) {
-        off[kSortBins - 1 - (tid * PB + i)] = run;
-        run += c[i];
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-        const uint32_t x = (uint32_t)__shfl_xor((int)big, o);
-        big = x > big ? x : big;
-    }
-    if (lane == 0) sh.wsum[tid >> 6] = big;
-    for (int e = tid; e < kSortBins; e += NT) cnt[e] = 0u;  // now insertion cursors
-    __syncthreads();
+    for (int w = 0; w < NWAVES; ++w) big = sh.wred[w][0] > big ? sh.wred[w][0] : big;
+    if (big > (uint32_t)kSortMaxBucket) {
+        // Degenerate: the whole buffer, with empty slots zeroed (below every
+        // real key), through a bitonic sort.
 #pragma unroll
-    for (int w = 0; w < NWAVES; ++w) big = sh.wsum[w] > big ? sh.wsum[w] : big;
-    __syncthreads();
-    if (big > (uint32_t)kSortMaxBucket) {  // uniform
-        bitonic_desc(cand, n, sh, tid);
+        for (int i = 0; i < PT; ++i) {
+            const int e = (i % PH) * NT + tid;
+            const bool inA = i < PH;
+            if (e >= (inA ? nA : nB)) cand[(inA ? 0 : kCapA) + e] = 0ull;
+        }
+        __syncthreads();
+        bitonic_desc(cand, kCand, tid);
         return;
     }
-    // Scatter into bucket order.
-    for (int e = tid; e < n; e += NT) {
-        const uint64_t key = cand[e];
-        const uint32_t b = bucket(key);
-        tmp[off[b] + atomicAdd(&cnt[b], 1u)] = key;
+#pragma unroll
+    for (int j = 0; j < PB; ++j) {
+        bk[kBuckets - 1 - (tid * PB + j)] = (run << 16) | c[j];
+        run += c[j];
     }
     __syncthreads();
-    // Place each key: its bucket's start plus the number of larger keys in it.
-    for (int e = tid; e < n; e += NT) {
-        const uint64_t key = tmp[e];
-        const uint32_t b = bucket(key);
-        const int o = (int)off[b], m = (int)cnt[b];
-        int rk = 0;
-        for (int q = o; q < o + m; ++q) rk += tmp[q] > key ? 1 : 0;
-        cand[o + rk] = key;
+    // Scatter into bucket order (every key is in registers).
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int e = (i % PH) * NT + tid;
+        if (e < (i < PH ? nA : nB)) cand[(bk[bkt[i]] >> 16) + slot[i]] = key[i];
     }
     __syncthreads();
-}
-
-// Appends the keys for which `take` holds to buf[*count...] (wave ballot,
-// one LDS atomic per wave).  `take` may differ per lane; every lane of the
-// block must call it the same number of times.
-__device__ inline void append(uint64_t *buf, uint32_t *count, bool take, uint64_t key, int lane)
-{
-    const uint64_t m = __ballot(take);
-    if (m == 0) return;  // wave-uniform: nothing to add
-    uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(count, (uint32_t)__popcll(m));
-    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
-    if (take) buf[base + lanes_below(m)] = key;
+    // Place inside the bucket: count the larger keys there.
+    uint32_t pos[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int e = (i % PH) * NT + tid;
+        pos[i] = 0u;
+        if (e < (i < PH ? nA : nB)) {
+            const uint32_t wd = bk[bkt[i]];
+            const int o = (int)(wd >> 16), m = (int)(wd & 0xFFFFu);
+            int rk = 0;
+            for (int q = o; q < o + m; ++q) rk += cand[q] > key[i] ? 1 : 0;
+            pos[i] = (uint32_t)(o + rk);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+        const int e = (i % PH) * NT + tid;
+        if (e < (i < PH ? nA : nB)) cand[pos[i]] = key[i];
+    }
+    __syncthreads();
 }
 
 // Row context shared by the selection strategies below.
 struct RowCtx {
-    const float *src;  // the row's chunk scores
+    const float *src;  // the row's chunk scores (a workspace row of clen floats)
     int64_t len;       // keys of this row in the chunk
     uint32_t c0;       // first key index of the chunk
-    bool filt;         // keys must beat u_floor (the running list is full)
-    uint32_t u_floor;
+    bool filt;         // keys must beat f_floor (the running list is full)
+    float f_floor;
 };
 
-// Reads the row's chunk scores in rounds of NT*16 (16 consecutive keys per
-// thread, vector loads), sorts each key into class 0 (dropped), 1 (-> bufa)
-// or 2 (-> bufb) with classify(score), and appends the kept keys to their
-// buffer in key-index order (a block-wide prefix sum per round gives every
-// thread its write offsets).  Returns the counts in na, nb.
-template <class F>
-__device__ void collect2(const RowCtx &r, F classify, uint64_t *bufa, uint64_t *bufb, int &na,
-                         int &nb, SelectShared &sh, int tid)
+// One streaming pass over the row's chunk scores, 16 consecutive keys per
+// thread per round, the next round's loads in flight while this round is
+// classified.  A key beating the floor goes to region A (cand[0..)) if its
+// score is >= f_sure, to region B (cand[kCapA..)) if it is >= f_edge, else it
+// is dropped.  Each wave reserves its slots with one LDS atomic per region
+// per round; the order inside a region is arbitrary (the sort fixes it).
+// Returns the region sizes (clamped to the capacities, which the callers'
+// counts never exceed).
+__device__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *cand,
+                        SelectShared &sh, int tid, int &nA, int &nB)
 {
     constexpr int V = 16;
-    na = 0;
-    nb = 0;
-    for (int64_t e0 = 0; e0 < r.len; e0 += (int64_t)NT * V) {
-        const int64_t base = e0 + (int64_t)tid * V;
-        float v[V];
-        if (base + V <= r.len) {
+    constexpr int ROUND = NT * V;
+    const int lane = tid & 63;
+    if (tid == 0) {
+        sh.nA = 0u;
+        sh.nB = 0u;
+    }
+    __syncthreads();
+    // Loads stay inside the workspace row: base is a multiple of 16 below
+    // len <= clen, and clen is a multiple of 256.
+    auto load = [&](float (&v)[V], int64_t base) {
+        if (base < r.len) {
 #pragma unroll
             for (int i = 0; i < V; i += 4) {
                 const float4 x = *(const float4 *)(r.src + base + i);
@@ -385,138 +480,100 @@ __device__ void collect2(const RowCtx &r, F classify, uint64_t *bufa, uint64_t *
                 v[i + 2] = x.z;
                 v[i + 3] = x.w;
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i) v[i] = base + i < r.len ? r.src[base + i] : 0.0f;
         }
+    };
+    auto process = [&](const float (&v)[V], int64_t base) {
         uint32_t cls = 0, cnt = 0;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            const uint32_t c = base + i < r.len ? classify(v[i]) : 0u;
+            const float x = v[i];
+            const bool ok = base + i < r.len && (!r.filt || x > r.f_floor);
+            const uint32_t c = !ok ? 0u : (x >= f_sure ? 1u : (x >= f_edge ? 2u : 0u));
             cls |= c << (2 * i);
             cnt += c == 1u ? 1u : (c == 2u ? 0x10000u : 0u);
         }
-        uint32_t total;
-        const uint32_t off = block_exclusive_sum(cnt, total, sh, tid);
-        int oa = na + (int)(off & 0xFFFFu), ob = nb + (int)(off >> 16);
+        const uint32_t incl = wave_incl_sum(cnt);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        if (tot == 0u) return;  // wave-uniform
+        uint32_t ba = 0, bb = 0;
+        if (lane == 0) {
+            if (tot & 0xFFFFu) ba = atomicAdd(&sh.nA, tot & 0xFFFFu);
+            if (tot >> 16) bb = atomicAdd(&sh.nB, tot >> 16);
+        }
+        const uint32_t excl = incl - cnt;
+        uint32_t pa = (uint32_t)__builtin_amdgcn_readfirstlane((int)ba) + (excl & 0xFFFFu);
+        uint32_t pb = (uint32_t)__builtin_amdgcn_readfirstlane((int)bb) + (excl >> 16);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const uint32_t c = (cls >> (2 * i)) & 3u;
             if (c != 0u) {
                 const uint64_t key = make_key(v[i], r.c0 + (uint32_t)(base + i));
-                if (c == 1u) bufa[oa++] = key;
-                else bufb[ob++] = key;
-            }
-        }
-        na += (int)(total & 0xFFFFu);
-        nb += (int)(total >> 16);
-    }
-    __syncthreads();
-}
-
-// Q = every chunk key that beats the floor (there are at most k of them).
-__device__ int collect_all(uint64_t *cand, const RowCtx &r, SelectShared &sh, int tid)
-{
-    const bool filt = r.filt;
-    const float f_floor = score_of_orderable(r.u_floor);
-    int na, nb;
-    collect2(r, [&](float x) -> uint32_t { return (!filt || x > f_floor) ? 1u : 0u; }, cand,
-             cand, na, nb, sh, tid);
-    return na;
-}
-
-// Q = the k best chunk keys that beat the floor, using the score kernel's
-// histogram summary: keys above bin b* are all in, keys in b* compete for the
-// remaining places by an exact radix select on their remaining bits.  The
-// bin edges are turned into fp32 thresholds (orderable() is monotone), so a
-// key is classified by two float compares.  When bin b* holds more keys than
-// the boundary buffer, one extra pass histograms the next 8 bits of the keys
-// in b* and narrows the boundary to one sub-bin.  Returns -1 if even the
-// sub-bin does not fit (massively tied scores); the caller falls back.
-__device__ int collect_by_bin(uint64_t *cand, const RowCtx &r, const ChunkMeta &mt, int k,
-                              SelectShared &sh, int tid)
-{
-    uint64_t *bnd = cand + k;  // boundary entries
-    const bool filt = r.filt;
-    const float f_floor = score_of_orderable(r.u_floor);
-    constexpr int BIN_SHIFT = 32 - kHistBits;  // orderable bits below the bin
-    uint32_t lo_u = mt.bin << BIN_SHIFT;        // boundary: orderable in [lo_u, hi_u)
-    uint32_t hi_u = (mt.bin + 1u) << BIN_SHIFT;
-    int need = k - (int)mt.above;
-    int first_shift = 64 - kHistBits - 8;
-    if (mt.in_bin > (uint32_t)kSelectPiece) {
-        // Histogram of orderable bits [BIN_SHIFT-8, BIN_SHIFT) inside bin b*.
-        sh.hist[tid] = 0u;
-        __syncthreads();
-        const float f_lo = mt.bin == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
-        const float f_hi = score_of_orderable(hi_u);
-        const int lane = tid & 63;
-        for (int64_t e0 = 0; e0 < r.len; e0 += NT) {
-            const int64_t e = e0 + tid;
-            bool in = false;
-            uint32_t d = 0;
-            if (e < r.len) {
-                const float x = r.src[e];
-                in = (!filt || x > f_floor) && x >= f_lo && !(x >= f_hi);
-                d = (orderable(x) >> (BIN_SHIFT - 8)) & 255u;
-            }
-            hist_add(sh.hist, in, d, lane);
-        }
-        __syncthreads();
-        if (tid < 64) {
-            uint32_t h4[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) h4[b] = sh.hist[4 * tid + b];
-            const uint32_t local = h4[0] + h4[1] + h4[2] + h4[3];
-            uint32_t incl = local;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t y = __shfl_down(incl, off);
-                if (tid + off < 64) incl += y;
-            }
-            uint32_t above = incl - local;
-#pragma unroll
-            for (int b = 3; b >= 0; --b) {
-                if (above < (uint32_t)need && (uint32_t)need <= above + h4[b]) {
-                    sh.digit = (uint32_t)(4 * tid + b);
-                    sh.above = above;
-                    sh.bin = h4[b];
+                if (c == 1u) {
+                    if (pa < (uint32_t)kCapA) cand[pa] = key;
+                    ++pa;
+                } else {
+                    if (pb < (uint32_t)kCapB) cand[kCapA + pb] = key;
+                    ++pb;
                 }
-                above += h4[b];
             }
         }
-        __syncthreads();
-        const uint32_t dsub = sh.digit;
-        need -= (int)sh.above;
-        const uint32_t sub_cnt = sh.bin;
-        __syncthreads();
-        if (sub_cnt > (uint32_t)kSelectPiece) return -1;
-        lo_u |= dsub << (BIN_SHIFT - 8);
-        hi_u = lo_u + (1u << (BIN_SHIFT - 8));
-        first_shift -= 8;
+    };
+    float cur[V], nxt[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) cur[i] = nxt[i] = 0.0f;
+    load(cur, (int64_t)tid * V);
+    for (int64_t e0 = 0; e0 < r.len; e0 += ROUND) {
+        load(nxt, e0 + ROUND + (int64_t)tid * V);
+        process(cur, e0 + (int64_t)tid * V);
+#pragma unroll
+        for (int i = 0; i < V; ++i) cur[i] = nxt[i];
     }
-    // Boundary edges as fp32 thresholds (bin 0 starts at -inf).
-    const float f_sure = score_of_orderable(hi_u);
-    const float f_edge = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
-    int above, in_bin;
-    collect2(
-        r,
-        [&](float x) -> uint32_t {
-            if (filt && !(x > f_floor)) return 0u;
-            return x >= f_sure ? 1u : (x >= f_edge ? 2u : 0u);
-        },
-        cand, bnd, above, in_bin, sh, tid);
-    need = k - above;
-    if (in_bin > need) radix_select(bnd, in_bin, need, sh, tid, first_shift);
-    for (int e = tid; e < need; e += NT) cand[above + e] = bnd[e];
     __syncthreads();
-    return k;
+    nA = (int)min(sh.nA, (uint32_t)kCapA);
+    nB = (int)min(sh.nB, (uint32_t)kCapB);
+    __syncthreads();
+}
+
+// Splits the boundary bin [lo_u, hi_u) (orderable values, width 2^shift)
+// by its next 8 bits: a histogram over the chunk keys in the bin that beat
+// the floor gives the sub-bin holding the need-th best of them.  Narrows
+// [lo_u, hi_u) to it and returns the keys above it inside the old bin.
+__device__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, uint32_t &hi_u, int shift,
+                               uint32_t need, uint32_t *hist, SelectShared &sh, int tid)
+{
+    const int lane = tid & 63;
+    hist[tid] = 0u;
+    __syncthreads();
+    const float f_lo = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
+    const float f_hi = score_of_orderable(hi_u);
+    const bool top = hi_u == 0u;  // the bin reaches the top of the orderable range
+    for (int64_t e0 = 0; e0 < r.len; e0 += NT) {
+        const int64_t e = e0 + tid;
+        bool in = false;
+        uint32_t d = 0;
+        if (e < r.len) {
+            const float x = r.src[e];
+            in = (!r.filt || x > r.f_floor) && x >= f_lo && (top || !(x >= f_hi));
+            d = (orderable(x) >> (shift - 8)) & 255u;
+        }
+        hist_add(hist, in, d, lane);
+    }
+    __syncthreads();
+    find_digit(hist, need, sh, tid);
+    __syncthreads();
+    const uint32_t above = sh.above;
+    lo_u |= sh.digit << (shift - 8);
+    hi_u = lo_u + (1u << (shift - 8));
+    __syncthreads();
+    return above;
 }
 
 // Q = the k best chunk keys that beat the floor, without a summary: the chunk
 // is read in pieces, keys that cannot enter the current best k are dropped,
 // and the candidates are cut back to k by radix select whenever they exceed k.
-__device__ int collect_pieces(uint64_t *cand, const RowCtx &r, int k, SelectShared &sh, int tid)
+// Leaves them, unsorted, in cand[0..count) and returns the count.
+__device__ int collect_pieces(uint64_t *cand, const RowCtx &r, int k, uint32_t *hist,
+                              SelectShared &sh, int tid)
 {
     const int lane = tid & 63;
     int cnt = 0;
@@ -531,17 +588,22 @@ __device__ int collect_pieces(uint64_t *cand, const RowCtx &r, int k, SelectShar
             bool take = false;
             uint64_t key = 0;
             if (e < plen) {
-                const uint32_t u = orderable(r.src[p0 + e]);
-                key = ((uint64_t)u << 32) |
-                      (uint64_t)(0xFFFFFFFFu - (r.c0 + (uint32_t)(p0 + e)));
-                take = (!r.filt || u > r.u_floor) && (!full || key > thr);
+                const float x = r.src[p0 + e];
+                key = make_key(x, r.c0 + (uint32_t)(p0 + e));
+                take = (!r.filt || x > r.f_floor) && (!full || key > thr);
             }
-            append(cand + cnt, &sh.count, take, key, lane);
+            const uint64_t m = __ballot(take);
+            if (m != 0) {  // wave-uniform
+                uint32_t base = 0;
+                if (lane == 0) base = atomicAdd(&sh.count, (uint32_t)__popcll(m));
+                base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+                if (take) cand[cnt + base + lanes_below(m)] = key;
+            }
         }
         __syncthreads();
         cnt += (int)sh.count;
         if (cnt > k) {
-            radix_select(cand, cnt, k, sh, tid);
+            radix_select(cand, cnt, k, hist, sh, tid);
             cnt = k;
         }
         if (cnt >= k) {
@@ -558,8 +620,8 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     extern __shared__ uint64_t smem[];
     __shared__ SelectShared sh;
     const int k = (int)a.k;
-    uint64_t *cand = smem;                      // k + kSelectPiece entries
-    uint64_t *lst = smem + k + kSelectPiece;    // k entries (running list)
+    uint64_t *cand = smem;                        // kCand keys
+    uint32_t *bk = (uint32_t *)(smem + kCand);    // kBuckets words (also a 256-bin histogram)
     const int tid = threadIdx.x;
     const int64_t rl = a.rows - 1 - (int64_t)blockIdx.x;  // long rows first
     const int64_t row = a.row0 + rl;
@@ -576,8 +638,6 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
         const RowState stt = a.state[rl];
         cnt_l = stt.count;
         theta = stt.theta;
-        const uint64_t *src = a.lists + rl * a.k;
-        for (int e = tid; e < cnt_l; e += NT) lst[e] = src[e];
     }
 
     RowCtx r;
@@ -585,39 +645,70 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
     r.len = len;
     r.c0 = (uint32_t)a.c0;
     r.filt = theta != 0;
-    r.u_floor = (uint32_t)(theta >> 32);
+    r.f_floor = score_of_orderable((uint32_t)(theta >> 32));
 
-    // Chunk-local best k (the partition step), sorted descending.
+    // Chunk-local best k (the partition step), sorted descending, in
+    // cand[0..cnt_q).
     int cnt_q = 0;
     if (len > 0) {
+        int nA = 0, nB = 0;
+        bool done = false;
         if (a.meta) {
             const ChunkMeta mt = a.meta[rl];
             if (mt.total <= (uint32_t)k) {
-                cnt_q = collect_all(cand, r, sh, tid);
+                // Every key that beats the floor (at most k of them).
+                collect(r, -__builtin_inff(), __builtin_inff(), cand, sh, tid, nA, nB);
+                done = true;
             } else {
-                cnt_q = collect_by_bin(cand, r, mt, k, sh, tid);
-                if (cnt_q < 0) cnt_q = collect_pieces(cand, r, k, sh, tid);
+                constexpr int BIN_SHIFT = 32 - kHistBits;  // orderable bits below the bin
+                uint32_t lo_u = mt.bin << BIN_SHIFT;        // boundary: orderable in [lo_u, hi_u)
+                uint32_t hi_u = (mt.bin + 1u) << BIN_SHIFT;
+                uint32_t in_bin = mt.in_bin;
+                bool fits = true;
+                if (in_bin > (uint32_t)kCapB) {
+                    const uint32_t need = (uint32_t)k - mt.above;
+                    const uint32_t up = refine_bin(r, lo_u, hi_u, BIN_SHIFT, need, bk, sh, tid);
+                    in_bin = sh.bin;
+                    fits = in_bin <= (uint32_t)kCapB;
+                    (void)up;
+                }
+                if (fits) {
+                    // Bin edges as fp32 thresholds (orderable() is monotone;
+                    // bin 0 starts at -inf, the top bin has no upper edge).
+                    const float f_sure = hi_u == 0u ? __builtin_nanf("") : score_of_orderable(hi_u);
+                    const float f_edge = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
+                    collect(r, f_sure, f_edge, cand, sh, tid, nA, nB);
+                    done = true;
+                }
             }
-        } else {
-            cnt_q = collect_pieces(cand, r, k, sh, tid);
         }
-    }
-    __syncthreads();
-    if (cnt_q > 1) {
-        uint64_t *tmp = cand + k;  // free once Q sits in cand[0..k)
-        uint32_t *bins = (uint32_t *)(smem + k + kSelectPiece + (a.first ? 0 : k));
-        if (cnt_q > 64) bucket_sort_desc(cand, tmp, cnt_q, bins, sh, tid);
-        else bitonic_desc(cand, cnt_q, sh, tid);
+        if (!done) {
+            // No summary (fp32 scores) or massively tied scores.
+            nA = collect_pieces(cand, r, k, bk, sh, tid);
+            nB = 0;
+        }
+        if (nA + nB > 1) sort_keys(cand, nA, nB, bk, sh, tid);
+        cnt_q = min(k, nA + nB);
     }
 
-    // Merge with the running list (both sorted descending) and write the
-    // first min(k, |L| + |Q|) entries: merge-path split per thread.
+    // Running list into the B region (free once the sort is done).
+    uint64_t *lst = cand + kCapA;
+    if (cnt_l > 0) {
+        const uint64_t *src = a.lists + rl * a.k;
+        for (int e = tid; e < cnt_l; e += NT) lst[e] = src[e];
+    }
+    __syncthreads();
+
+    // Merge with the running list (both sorted descending) and keep the
+    // first min(k, |L| + |Q|) entries: merge-path split, 8 outputs per thread.
     const int total = min(k, cnt_l + cnt_q);
     constexpr int PT = (2048 + NT - 1) / NT;  // outputs per thread (k <= 2048)
     const int p0 = tid * PT;
     uint64_t outv[PT];
     uint64_t kth = 0;  // the entry at position k-1, for the next chunk's floor
     int nout = 0;
+#pragma unroll
+    for (int t = 0; t < PT; ++t) outv[t] = 0ull;
     if (p0 < total) {
         int lo = max(0, p0 - cnt_q), hi = min(p0, cnt_l);
         while (lo < hi) {  // i = entries taken from L before position p0
@@ -626,35 +717,60 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
             else hi = mid;
         }
         int i = lo, j = p0 - lo;
+#pragma unroll
         for (int t = 0; t < PT; ++t) {
-            if (p0 + t >= total) break;
-            uint64_t v;
-            if (j >= cnt_q || (i < cnt_l && lst[i] > cand[j])) v = lst[i++];
-            else v = cand[j++];
-            outv[t] = v;
-            if (p0 + t == k - 1) kth = v;
-            ++nout;
+            if (p0 + t < total) {
+                uint64_t v;
+                if (j >= cnt_q || (i < cnt_l && lst[i] > cand[j])) v = lst[i++];
+                else v = cand[j++];
+                outv[t] = v;
+                if (p0 + t == k - 1) kth = v;
+                ++nout;
+            }
         }
     }
     if (a.emit) {
         int32_t *oi = a.out_idx + row * a.k;
         float *os = a.out_score + row * a.k;
+        int32_t vi[PT];
+        float vs[PT];
+#pragma unroll
         for (int t = 0; t < PT; ++t) {
-            const int p = p0 + t;
-            if (p >= k) break;
-            if (t < nout) {
-                oi[p] = key_index(outv[t]);
-                os[p] = key_score(outv[t]);
-            } else {
-                oi[p] = -1;
-                os[p] = -__builtin_inff();
+            vi[t] = t < nout ? key_index(outv[t]) : -1;
+            vs[t] = t < nout ? key_score(outv[t]) : -__builtin_inff();
+        }
+        const bool al16 = ((((uintptr_t)oi) | ((uintptr_t)os)) & 15u) == 0u;
+        if (al16 && p0 + PT <= k) {  // 16-byte aligned, whole
+#pragma unroll
+            for (int t = 0; t < PT; t += 4) {
+                *(int4 *)(oi + p0 + t) = make_int4(vi[t], vi[t + 1], vi[t + 2], vi[t + 3]);
+                *(float4 *)(os + p0 + t) = make_float4(vs[t], vs[t + 1], vs[t + 2], vs[t + 3]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < PT; ++t) {
+                if (p0 + t < k) {
+                    oi[p0 + t] = vi[t];
+                    os[p0 + t] = vs[t];
+                }
             }
         }
-        // Rows with k > 2048 do not exist (k <= CSA_MAX_K); positions beyond
-        // NT*PT are covered because NT*PT >= k.
+        // NT*PT >= k (k <= CSA_MAX_K = 2048), so every position is written.
     } else {
         uint64_t *dst = a.lists + rl * a.k;
-        for (int t = 0; t < nout; ++t) dst[p0 + t] = outv[t];
+        if ((k & 1) == 0 && p0 + PT <= total) {  // 16-byte aligned, whole
+#pragma unroll
+            for (int t = 0; t < PT; t += 2) {
+                ulonglong2 v2;
+                v2.x = outv[t];
+                v2.y = outv[t + 1];
+                *(ulonglong2 *)(dst + p0 + t) = v2;
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < PT; ++t)
+                if (t < nout) dst[p0 + t] = outv[t];
+        }
         if (total == k && p0 <= k - 1 && k - 1 < p0 + nout) a.state[rl].theta = kth;
         if (tid == 0) {
             a.state[rl].count = total;
@@ -668,8 +784,7 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0) return hipSuccess;
-    const size_t entries = (size_t)(a.k + kSelectPiece) + (a.first ? 0 : (size_t)a.k);
-    const size_t lds = entries * sizeof(uint64_t) + 2 * kSortBins * sizeof(uint32_t);
+    const size_t lds = (size_t)kCand * sizeof(uint64_t) + (size_t)kBuckets * sizeof(uint32_t);
     select_kernel<<<dim3((unsigned)a.rows), dim3(NT), lds, stream>>>(a);
     return hipGetLastError();
 }

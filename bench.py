@@ -15,6 +15,8 @@ oracle timed on a bounded sample of the same workload's rows on the host.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
@@ -35,11 +37,87 @@ METRIC = "scored q-k pairs/s at S=65536 V4-Flash dims; MFMA util %; peak HBM GB"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_BUSY_PEAK = MFMA_BF16_PEAK_TFLOPS
 HBM_PEAK_GBS = 8000.0
+# HBM traffic of the score kernel, summarised from two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE) of the default workload by --traffic-from.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_bf16_S65536_hbm_traffic.txt")
+SCORE_SOURCES = ("streaming_indexer_top_amd/csrc/score_kernels.hip",
+                 "streaming_indexer_top_amd/csrc/csa_internal.h")
 
 
 def pair_count(S, T, m, q_pos0=0):
     i = np.arange(S, dtype=np.int64) + q_pos0
     return int(np.minimum(T, (i + 1) // m).sum())
+
+
+def score_source_hash():
+    """sha256 over the sources that define the score kernel."""
+    h = hashlib.sha256()
+    for rel in SCORE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """Per-launch HBM bytes of the score kernel from TRAFFIC_FILE, or None when
+    the file is missing or was taken from other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(":", 1) for l in f if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    kv = {a.strip(): b.strip() for a, b in kv.items()}
+    if kv.get("source_sha256") != score_source_hash():
+        return None
+    return {"bytes": float(kv["traffic_bytes_per_launch"]),
+            "fetch": float(kv["fetch_bytes_per_launch"]),
+            "write": float(kv["write_bytes_per_launch"])}
+
+
+def summarize_counters(fetch_csv, write_csv, copy_bytes):
+    """Summary text for TRAFFIC_FILE from the counter CSVs of two rocprofv3 runs
+    of `bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-probe B` (one with
+    --pmc FETCH_SIZE, one with --pmc WRITE_SIZE).  Each counter is scaled by
+    what it reads for the probe's plain device copy of B bytes."""
+    def load(path, counter):
+        with open(path) as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        pick = lambda tag: [float(r["Counter_Value"]) for r in rows if tag in r["Kernel_Name"]]
+        copy = pick("copyBuffer")
+        if len(copy) != 1:
+            raise SystemExit("%s: expected one copy-probe dispatch, found %d" % (path, len(copy)))
+        return pick("score_bf16_kernel"), pick("select_kernel"), copy[0]
+    f_sc, f_se, f_cp = load(fetch_csv, "FETCH_SIZE")
+    w_sc, w_se, w_cp = load(write_csv, "WRITE_SIZE")
+    if not f_sc or len(f_sc) != len(w_sc):
+        raise SystemExit("score kernel dispatches differ between the two runs")
+    true_kib = copy_bytes / 1024.0
+    ff, wf = true_kib / f_cp, true_kib / w_cp
+    n = len(f_sc)
+    fetch = sum(f_sc) * ff * 1024.0 / n
+    write = sum(w_sc) * wf * 1024.0 / n
+    out = [
+        "source_sha256: %s" % score_source_hash(),
+        "calibration_copy_bytes: %d" % copy_bytes,
+        "calibration_copy_fetch_kib_raw: %.3f" % f_cp,
+        "calibration_copy_write_kib_raw: %.3f" % w_cp,
+        "fetch_factor: %.6f" % ff,
+        "write_factor: %.6f" % wf,
+        "score_launches: %d" % n,
+        "score_fetch_kib_raw: %s" % " ".join("%.3f" % x for x in f_sc),
+        "score_write_kib_raw: %s" % " ".join("%.3f" % x for x in w_sc),
+        "fetch_bytes_per_launch: %.0f" % fetch,
+        "write_bytes_per_launch: %.0f" % write,
+        "traffic_bytes_per_launch: %.0f" % (fetch + write),
+    ]
+    if f_se and len(f_se) == len(w_se):
+        m = len(f_se)
+        out += [
+            "select_launches: %d" % m,
+            "select_fetch_bytes_per_launch: %.0f" % (sum(f_se) * ff * 1024.0 / m),
+            "select_write_bytes_per_launch: %.0f" % (sum(w_se) * wf * 1024.0 / m),
+        ]
+    return "\n".join(out) + "\n"
 
 
 def make_inputs(cfg_n, dev):
@@ -92,50 +170,55 @@ def cpu_baseline(q, w, kc, m, k, S, T, target_s, max_rows, seed):
 
 
 def run_sweep(args, q, w, kc, c, dev, base_alloc):
-    """Chunk-size x key-tile sweep: time per call, throughput, peak HBM, and a
-    bit-identity check of every setting's outputs against the first one's."""
-    S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    """Top-k x chunk-size x key-tile sweep: time per call, throughput, peak HBM,
+    and a bit-identity check of every setting's outputs against the first
+    setting with the same k."""
+    S, T, H, D, m = c["S"], c["T"], c["H"], c["D"], c["m"]
     P = pair_count(S, T, m)
-    idx = torch.empty((S, k), dtype=torch.int32, device=dev)
-    score = torch.empty((S, k), dtype=torch.float32, device=dev)
-    ref = None
-    for chunk in [int(x) for x in args.sweep_chunks.split(",")]:
-        for tile in [int(x) for x in args.sweep_tiles.split(",")]:
-            ws_bytes = csa.workspace_size(S, T, H, D, m, k, chunk_keys=chunk, key_tile=tile,
-                                          workspace_budget=args.budget)
-            torch.cuda.reset_peak_memory_stats(dev)
-            workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-            kw = dict(chunk_keys=chunk, key_tile=tile, workspace_budget=args.budget,
-                      workspace=workspace, out=(idx, score))
-            for _ in range(args.warmup):
-                csa.topk(q, w, kc, m, k, **kw)
-            torch.cuda.synchronize()
-            csa.profile_collect()
-            csa.profile_enable(True)
-            t0 = time.perf_counter()
-            for _ in range(args.steps):
-                csa.topk(q, w, kc, m, k, **kw)
-            torch.cuda.synchronize()
-            t1 = time.perf_counter()
-            csa.profile_enable(False)
-            prof = csa.profile_collect()
-            ms = (t1 - t0) * 1e3 / args.steps
-            if ref is None:
-                ref = (idx.clone(), score.clone())
-                same = True
-            else:
-                same = bool(torch.equal(ref[0], idx)) and bool(
-                    torch.equal(ref[1].view(torch.int32), score.view(torch.int32)))
-            peak = torch.cuda.max_memory_allocated(dev) - base_alloc
-            print(json.dumps({
-                "workload": args.workload, "S": S, "T": T, "chunk_keys": chunk, "key_tile": tile,
-                "ms_per_call": ms, "pairs_per_s": P / (ms * 1e-3),
-                "mfma_util_pct": 100.0 * P * 2 * H * D / (ms * 1e-3) / (MFMA_BUSY_PEAK * 1e12),
-                "score_ms": prof["score"][0] / args.steps, "select_ms": prof["select"][0] / args.steps,
-                "score_launches": prof["score"][1] / args.steps,
-                "workspace_bytes": ws_bytes, "peak_hbm_gib": peak / 2 ** 30,
-                "bit_identical_to_first": same}), flush=True)
-            del workspace
+    ks = [int(x) for x in args.sweep_ks.split(",")] if args.sweep_ks else [c["k"]]
+    for k in ks:
+        idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+        score = torch.empty((S, k), dtype=torch.float32, device=dev)
+        ref = None
+        for chunk in [int(x) for x in args.sweep_chunks.split(",")]:
+            for tile in [int(x) for x in args.sweep_tiles.split(",")]:
+                ws_bytes = csa.workspace_size(S, T, H, D, m, k, chunk_keys=chunk, key_tile=tile,
+                                              workspace_budget=args.budget)
+                torch.cuda.reset_peak_memory_stats(dev)
+                workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+                kw = dict(chunk_keys=chunk, key_tile=tile, workspace_budget=args.budget,
+                          workspace=workspace, out=(idx, score))
+                for _ in range(args.warmup):
+                    csa.topk(q, w, kc, m, k, **kw)
+                torch.cuda.synchronize()
+                csa.profile_collect()
+                csa.profile_enable(True)
+                t0 = time.perf_counter()
+                for _ in range(args.steps):
+                    csa.topk(q, w, kc, m, k, **kw)
+                torch.cuda.synchronize()
+                t1 = time.perf_counter()
+                csa.profile_enable(False)
+                prof = csa.profile_collect()
+                ms = (t1 - t0) * 1e3 / args.steps
+                if ref is None:
+                    ref = (idx.clone(), score.clone())
+                    same = True
+                else:
+                    same = bool(torch.equal(ref[0], idx)) and bool(
+                        torch.equal(ref[1].view(torch.int32), score.view(torch.int32)))
+                peak = torch.cuda.max_memory_allocated(dev) - base_alloc
+                print(json.dumps({
+                    "workload": args.workload, "S": S, "T": T, "k": k, "chunk_keys": chunk,
+                    "key_tile": tile, "ms_per_call": ms, "pairs_per_s": P / (ms * 1e-3),
+                    "mfma_util_pct": 100.0 * P * 2 * H * D / (ms * 1e-3) / (MFMA_BUSY_PEAK * 1e12),
+                    "score_ms": prof["score"][0] / args.steps,
+                    "select_ms": prof["select"][0] / args.steps,
+                    "score_launches": prof["score"][1] / args.steps,
+                    "workspace_bytes": ws_bytes, "peak_hbm_gib": peak / 2 ** 30,
+                    "bit_identical_to_first": same}), flush=True)
+                del workspace
+        del idx, score
 
 
 def main():
@@ -148,18 +231,29 @@ def main():
     ap.add_argument("--tile", type=int, default=0)
     ap.add_argument("--budget", type=int, default=0, help="workspace budget in bytes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--cpu-max-rows", type=int, default=4096)
+    ap.add_argument("--cpu-max-rows", type=int, default=12288)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
-                    help="time every chunk x key-tile setting (default grid: chunk 4096..65536, "
-                         "tile 64/128/256), one JSON line each, checking that all settings give "
-                         "bit-identical outputs")
+                    help="time every (top-k x) chunk x key-tile setting (default grid: chunk "
+                         "4096..65536, tile 64/128/256), one JSON line each, checking that all "
+                         "settings with the same k give bit-identical outputs")
     ap.add_argument("--sweep-chunks", default="4096,8192,16384,32768,65536")
     ap.add_argument("--sweep-tiles", default="64,128,256")
+    ap.add_argument("--sweep-ks", default="", help="top-k values to sweep (default: the workload's k)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device copy run once before timing, as a known "
                          "reference for HBM traffic counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc runs "
+                         "(needs --copy-probe with the probe size those runs used); no GPU")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        if not args.copy_probe:
+            raise SystemExit("--traffic-from needs --copy-probe BYTES")
+        sys.stdout.write(summarize_counters(args.traffic_from[0], args.traffic_from[1],
+                                            args.copy_probe))
+        return
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this path runs on a single MI355X and has no "
@@ -226,6 +320,10 @@ def main():
     per_launch_ms = score_ms / max(score_n, 1)
     flops_per_launch = flops / max(score_n / args.steps, 1)
     achieved = flops_per_launch / (per_launch_ms * 1e-3) / 1e12 if score_n else 0.0
+    # Counter figures hold for the workload and plan they were taken on.
+    traffic = None
+    if args.workload == 3 and not (args.chunk or args.tile or args.budget):
+        traffic = read_traffic()
 
     out = {
         "metric": METRIC,
@@ -253,7 +351,9 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": traffic["bytes"] if traffic else None,
+            "traffic_fetch_write": [traffic["fetch"], traffic["write"]] if traffic else None,
+            "traffic_per": "launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy)",
             "kernel": "score_bf16_kernel",
             "launch_ms": per_launch_ms,
             "launches_per_step": score_n / args.steps,

@@ -217,7 +217,8 @@ def test_repeat_runs_bit_identical():
 
 # ------------------------------------------------- full workload shapes ----
 
-def _full_shape_check(cfg_n, kc_kind="gaussian", sample=None, integer=False, seed=None):
+def _full_shape_check(cfg_n, kc_kind="gaussian", sample=None, integer=False, seed=None,
+                      shard_tail=0):
     c = inputs.config(cfg_n)
     S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
     seed = cfg_n if seed is None else seed
@@ -234,6 +235,16 @@ def _full_shape_check(cfg_n, kc_kind="gaussian", sample=None, integer=False, see
     q, w, kc = q.to(DEV), w.to(DEV), kc.to(DEV)
     idx, sc = csa.topk(q, w, kc, m, k)
     torch.cuda.synchronize()
+    if shard_tail:
+        # The last rows on their own (the heaviest shard of a row-sharded
+        # run): q_pos0 places them, and the outputs must equal the full run's.
+        R = shard_tail
+        s_idx, s_sc = csa.topk(q[S - R:], w[S - R:], kc, m, k, q_pos0=S - R)
+        torch.cuda.synchronize()
+        assert torch.equal(s_idx, idx[S - R:])
+        assert torch.equal(s_sc.view(torch.int32), sc[S - R:].view(torch.int32))
+        say("  tail shard of %d rows with q_pos0=%d identical to the full run" % (R, S - R))
+        del s_idx, s_sc
     rows = np.arange(S) if sample is None else np.array(inputs.sample_rows(S, m, k, sample, seed))
     rows_t = torch.from_numpy(rows).to(DEV)
     g_idx = idx[rows_t].cpu().numpy()
@@ -276,4 +287,4 @@ def test_cfg4_mixture_sampled():
 
 @pytest.mark.slow
 def test_cfg5_sampled():
-    _full_shape_check(5, sample=64)
+    _full_shape_check(5, sample=256, shard_tail=8192)

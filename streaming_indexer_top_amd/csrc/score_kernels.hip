@@ -40,6 +40,22 @@ __device__ inline float key_score_of(uint32_t u)
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
+// Buffer resource of `bytes` bytes at `base` (raw, stride 0); accesses at
+// or beyond `bytes` read 0 and write nothing.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// orderable() for scores that are never -0: every score here is a sum that
+// starts at +0, and under round-to-nearest such a sum is never -0.
+__device__ inline uint32_t orderable_nz(float s)
+{
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // ReLU on the bit pattern: a float with the sign bit set is a negative
 // integer, so an integer max with 0 maps every negative score (and -0) to +0
 // and leaves the rest unchanged, in one instruction and with no NaN quieting.
@@ -164,22 +180,21 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     // groups.  The next tile is loaded into registers while the current one
     // is computed and written to LDS after it.  (LDS DMA would save these
     // registers, but then every LDS histogram update would wait for all
-    // outstanding global memory operations.)  Keys past the last usable one
-    // read a clamped (valid, unused) key.
+    // outstanding global memory operations.)  Each tile is read through a
+    // buffer resource that ends at the last usable key, so the per-thread
+    // offsets are constants and keys past the end read as zeros (their
+    // scores are never used).
     constexpr int NCHUNK = NT * CH;                // 16-byte chunks per tile
     constexpr int PER = (NCHUNK + THREADS - 1) / THREADS;      // chunks per thread
     u32x4 st[PER];
     auto gload = [&](int t) {
         const int64_t base = kb0 + (int64_t)t * NT;
+        const int64_t nk = min((int64_t)NT, k_end - base);
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc((const uint16_t *)a.kc + base * D, (uint32_t)(nk * ROWB));
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int c = min(p * THREADS + tid, NCHUNK - 1);
-            const int key = c / CH;
-            const int ch = c % CH;
-            int64_t gk = base + key;
-            gk = gk < k_end ? gk : k_end - 1;
-            st[p] = *(const u32x4 *)((const uint16_t *)a.kc + gk * D + ch * 8);
-        }
+        for (int p = 0; p < PER; ++p)
+            st[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (p * THREADS + tid) * 16, 0, 0);
     };
     auto lstore = [&](int buf) {
 #pragma unroll
@@ -222,6 +237,7 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     // Scores are stored and counted 64 keys at a time (2 blocks): chunk-
     // relative 32-bit key offsets, one lane per key.
     float *wsrow = a.ws + (active ? rl : 0) * a.clen;
+    const __amdgpu_buffer_rsrc_t ws_rs = buffer_rsrc(wsrow, (uint32_t)(a.clen * 4));
     const int my_len = (int)(my_end - kb0);  // keys of this row in the chunk
     const float f_floor = filt ? key_score_of(u_floor) : 0.0f;
     uint32_t *h = hist_all + wave * kHistBins;
@@ -251,9 +267,9 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         const float sc = __uint_as_float(z[0]) + __uint_as_float(z[1]);
         const int rel = rel0 + lane;
         const bool valid = real && rel < my_len;
-        wsrow[rel] = sc;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), ws_rs, lane * 4, rel0 * 4, 0);
         const uint32_t inc = (valid && (!filt || sc > f_floor)) ? 1u : 0u;
-        atomicAdd(&h[orderable(sc) >> (32 - kHistBits)], inc);
+        atomicAdd(&h[orderable_nz(sc) >> (32 - kHistBits)], inc);
     };
 
     // The last block of a tile is finished under the first block's MFMAs of

@@ -48,6 +48,15 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t 
                                              0x00020000);
 }
 
+// One 16-byte LDS DMA per lane: bytes [off, off+16) of the buffer land at
+// dst + 16*lane (dst wave-uniform).  A plain device function: inside a
+// lambda of the kernel template the host pass drops the kernel's stub.
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16,
+                                            off, 0, 0, 0);
+}
+
 // orderable() for scores that are never -0: every score here is a sum that
 // starts at +0, and under round-to-nearest such a sum is never -0.
 __device__ inline uint32_t orderable_nz(float s)
@@ -99,12 +108,15 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     constexpr int ROWB = D * 2;        // bytes per key row
     constexpr int TILEB = NT * ROWB;   // bytes per LDS tile
     constexpr int NB = NT / 32;        // 32-key blocks per tile
-    constexpr int NBUF = DB ? 2 : 1;
     static_assert(NB % 2 == 0, "blocks are finished in pairs");
-    // Dynamic LDS: [NBUF key tiles][8 row histograms].
+    // LDS: double-buffered key tiles are two static arrays (so that the
+    // compiler can tell the tile being read from the tile being filled by
+    // DMA); the row histograms, and the single-buffered tile, are dynamic.
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ __attribute__((aligned(16))) unsigned char tile_a[DB ? TILEB : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char tile_b[DB ? TILEB : 16];
     unsigned char *lds = smem;
-    uint32_t *hist_all = (uint32_t *)(smem + NBUF * TILEB);
+    uint32_t *hist_all = (uint32_t *)(smem + (DB ? 0 : TILEB));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -196,6 +208,32 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         for (int p = 0; p < PER; ++p)
             st[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (p * THREADS + tid) * 16, 0, 0);
     };
+    // Double-buffered tiles are filled by LDS DMA: each wave moves 1 KiB
+    // pieces, lane l of a piece landing at byte 16*l of it.  The lane loads
+    // the global chunk that the swizzled layout puts there, so the tile in
+    // LDS is the same as with register staging, without staging registers or
+    // LDS writes.
+    constexpr int NPIECE = TILEB / 1024;
+    constexpr int PIECES_W = (NPIECE + WAVES - 1) / WAVES;  // pieces per wave
+    int dma_off[PIECES_W];
+#pragma unroll
+    for (int j = 0; j < PIECES_W; ++j) {
+        const int pos = (j * WAVES + wave) * 1024 + lane * 16;  // byte in the tile
+        const int key = pos / ROWB;
+        const int slot = (pos % ROWB) >> 4;
+        dma_off[j] = key * ROWB + ((slot ^ (key & (CH - 1))) << 4);
+    }
+    auto dma = [&](unsigned char *dst, int t) {
+        const int64_t base = kb0 + (int64_t)t * NT;
+        const int64_t nk = min((int64_t)NT, k_end - base);
+        const __amdgpu_buffer_rsrc_t rs =
+            buffer_rsrc((const uint16_t *)a.kc + base * D, (uint32_t)(nk * ROWB));
+#pragma unroll
+        for (int j = 0; j < PIECES_W; ++j) {
+            if (j * WAVES + wave < NPIECE)  // wave-uniform
+                dma16(rs, dst + (j * WAVES + wave) * 1024, dma_off[j]);
+        }
+    };
     auto lstore = [&](int buf) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
@@ -269,7 +307,11 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         const bool valid = real && rel < my_len;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), ws_rs, lane * 4, rel0 * 4, 0);
         const uint32_t inc = (valid && (!filt || sc > f_floor)) ? 1u : 0u;
-        atomicAdd(&h[orderable_nz(sc) >> (32 - kHistBits)], inc);
+        // A plain LDS atomic here would make the compiler wait for every
+        // tile DMA in flight; the add does not touch the tiles.
+        const uint32_t hp = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)(
+            h + (orderable_nz(sc) >> (32 - kHistBits)));
+        asm volatile("ds_add_u32 %0, %1" ::"v"(hp), "v"(inc));
     };
 
     // The last block of a tile is finished under the first block's MFMAs of
@@ -293,15 +335,9 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         pend = false;
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const bool more = t + 1 < ntiles;
-        if (more) gload(t + 1);
+    auto compute_tile = [&](const unsigned char *tb, int t) {
         const int rel_t = t * NT;  // tile start relative to the chunk
         if (active && rel_t < my_len) {
-            const unsigned char *tb = lds + (DB ? (t & 1) * TILEB : 0);
             bf16x8 bb[2][HALF];
             float pacc = 0.0f;  // share of the block being finished
             float pe = 0.0f;    // share of the even block of the current pair
@@ -331,11 +367,38 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         } else if (pend) {
             flush();
         }
-        if (more) {
-            if constexpr (!DB) __syncthreads();  // single buffer: all reads done
-            lstore(DB ? ((t + 1) & 1) : 0);
-        }
+    };
+
+    if constexpr (DB) {
+        // Tile t+1 is DMA'd into the other buffer while tile t is computed;
+        // the barrier after each tile (whose fence waits for the DMA) makes
+        // the new tile visible and frees the old one.  Unrolled by two so
+        // that every access names its buffer at compile time.
+        dma(tile_a, 0);
         __syncthreads();
+        for (int t = 0; t < ntiles; t += 2) {
+            if (t + 1 < ntiles) dma(tile_b, t + 1);
+            compute_tile(tile_a, t);
+            __syncthreads();
+            if (t + 1 >= ntiles) break;
+            if (t + 2 < ntiles) dma(tile_a, t + 2);
+            compute_tile(tile_b, t + 1);
+            __syncthreads();
+        }
+    } else {
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int t = 0; t < ntiles; ++t) {
+            const bool more = t + 1 < ntiles;
+            if (more) gload(t + 1);
+            compute_tile(lds, t);
+            if (more) {
+                __syncthreads();  // single buffer: all reads done
+                lstore(0);
+            }
+            __syncthreads();
+        }
     }
     if (pend) flush();
 
@@ -417,9 +480,12 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a)
 template <int D, int HT, int NT, bool DB, int WAVES>
 hipError_t launch_bf16_cfg(const ScoreArgs &a, hipStream_t s)
 {
-    constexpr size_t lds = (DB ? 2 : 1) * (size_t)NT * D * 2 +
+    // Dynamic part: the histograms, plus the tile when single-buffered (the
+    // double-buffered tiles are static arrays of the kernel).
+    constexpr size_t lds = (DB ? 0 : (size_t)NT * D * 2) +
                            (size_t)WAVES * kHistBins * sizeof(uint32_t);
-    static_assert(lds <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+    static_assert(lds + (DB ? 2 * (size_t)NT * D * 2 : 0) <= 160 * 1024,
+                  "LDS budget of a gfx950 workgroup");
     static bool attr_set = false;  // benign race: every caller sets the same value
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)score_bf16_kernel<D, HT, NT, DB, WAVES>,

@@ -211,12 +211,31 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
         if (!workspace) return CSA_ERR_NULL_PTR;
         rows = rows_fitting(p, S, k, workspace_bytes);
         if (rows <= 0) return CSA_ERR_WORKSPACE_TOO_SMALL;
-        // Same number of passes, rows spread evenly over them (a pass of a
-        // few rows would run on a handful of CUs).
-        const int64_t passes = (S + rows - 1) / rows;
-        int64_t even = (S + passes - 1) / passes;
-        even = (even + csa::kScoreWaves - 1) / csa::kScoreWaves * csa::kScoreWaves;
-        if (even < rows) rows = even;
+        if (rows < S) {
+            // Several passes.  Score workgroups of one pass run in rounds of
+            // (CUs x workgroups per CU); a partial round leaves CUs idle for
+            // a whole workgroup's time, so passes get whole rounds (only the
+            // last pass has a partial one).  Without a round size (fp32, or
+            // the queries fail), rows are spread evenly over the passes so
+            // that no pass is a handful of rows on a handful of CUs.
+            int dev = 0, ncu = 0;
+            int64_t round_rows = 0;
+            if (hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) ==
+                    hipSuccess) {
+                const int bpc = csa::score_blocks_per_cu(dtype, D_I, H_I, p.tile);
+                round_rows = (int64_t)ncu * bpc * csa::kScoreWaves;
+            }
+            if (round_rows <= 0) (void)hipGetLastError();  // a failed query is not a launch error
+            if (round_rows > 0 && rows >= round_rows) {
+                rows = rows / round_rows * round_rows;
+            } else {
+                const int64_t passes = (S + rows - 1) / rows;
+                int64_t even = (S + passes - 1) / passes;
+                even = (even + csa::kScoreWaves - 1) / csa::kScoreWaves * csa::kScoreWaves;
+                if (even < rows) rows = even;
+            }
+        }
     }
     hipStream_t s = (hipStream_t)stream;
 

@@ -89,6 +89,10 @@ enum { DT_F32 = 0, DT_BF16 = 1 };
 hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t key_tile,
                         hipStream_t stream);
 
+// Score workgroups that one CU runs at once (bf16 path; 0 for fp32 or on
+// error), for sizing passes in whole rounds of workgroups.
+int score_blocks_per_cu(int32_t dtype, int32_t D, int32_t H, int32_t key_tile);
+
 // Select kernel: one workgroup per row of the batch.
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 

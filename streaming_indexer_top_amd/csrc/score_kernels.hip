@@ -498,6 +498,30 @@ hipError_t launch_bf16_cfg(const ScoreArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int D, int HT, int NT, bool DB, int WAVES>
+int blocks_per_cu_cfg()
+{
+    constexpr size_t lds = (DB ? 0 : (size_t)NT * D * 2) +
+                           (size_t)WAVES * kHistBins * sizeof(uint32_t);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, (const void *)score_bf16_kernel<D, HT, NT, DB, WAVES>, WAVES * 64, lds) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
+template <int D, int HT>
+int blocks_per_cu_tile(int32_t key_tile)
+{
+    switch (key_tile) {
+    case 64: return blocks_per_cu_cfg<D, HT, 64, true, 8>();
+    case 128: return blocks_per_cu_cfg<D, HT, 128, true, 8>();
+    case 256: return blocks_per_cu_cfg<D, HT, 256, (D < 128), 8>();
+    default: return 0;
+    }
+}
+
 template <int D, int HT>
 hipError_t launch_bf16_tile(const ScoreArgs &a, int32_t key_tile, hipStream_t s)
 {
@@ -520,6 +544,19 @@ hipError_t launch_bf16_d(const ScoreArgs &a, int32_t key_tile, hipStream_t s)
 }
 
 }  // namespace
+
+int score_blocks_per_cu(int32_t dtype, int32_t D, int32_t H, int32_t key_tile)
+{
+    if (dtype != DT_BF16) return 0;
+    const bool two = H > 32;
+    switch (D) {
+    case 32: return two ? blocks_per_cu_tile<32, 2>(key_tile) : blocks_per_cu_tile<32, 1>(key_tile);
+    case 64: return two ? blocks_per_cu_tile<64, 2>(key_tile) : blocks_per_cu_tile<64, 1>(key_tile);
+    case 128:
+        return two ? blocks_per_cu_tile<128, 2>(key_tile) : blocks_per_cu_tile<128, 1>(key_tile);
+    default: return 0;
+    }
+}
 
 hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t key_tile,
                         hipStream_t stream)

@@ -298,7 +298,7 @@ __device__ void bitonic_desc(uint64_t *cand, int n, int tid)
 // larger keys there.  If a bucket holds more than kSortMaxBucket keys (many
 // equal or clustered scores) a bitonic sort of the whole buffer takes over.
 // bk: kBuckets words.
-__device__ void sort_keys(uint64_t *cand, int nA, int nB, uint32_t *bk, SelectShared &sh,
+__device__ __forceinline__ void sort_keys(uint64_t *cand, int nA, int nB, uint32_t *bk, SelectShared &sh,
                           int tid)
 {
     const int lane = tid & 63;
@@ -449,15 +449,32 @@ struct RowCtx {
     float f_floor;
 };
 
+// Loads 16 consecutive scores of a workspace row at `base` if base < len.
+// Stays inside the row: base is a multiple of 16 below len <= clen, and clen
+// is a multiple of 256.
+__device__ inline void load16(const float *src, int64_t len, int64_t base, float (&v)[16])
+{
+    if (base < len) {
+#pragma unroll
+        for (int i = 0; i < 16; i += 4) {
+            const float4 x = *(const float4 *)(src + base + i);
+            v[i] = x.x;
+            v[i + 1] = x.y;
+            v[i + 2] = x.z;
+            v[i + 3] = x.w;
+        }
+    }
+}
+
 // One streaming pass over the row's chunk scores, 16 consecutive keys per
-// thread per round, the next round's loads in flight while this round is
+// thread per round, the next two rounds' loads in flight while this round is
 // classified.  A key beating the floor goes to region A (cand[0..)) if its
 // score is >= f_sure, to region B (cand[kCapA..)) if it is >= f_edge, else it
 // is dropped.  Each wave reserves its slots with one LDS atomic per region
 // per round; the order inside a region is arbitrary (the sort fixes it).
 // Returns the region sizes (clamped to the capacities, which the callers'
 // counts never exceed).
-__device__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *cand,
+__device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *cand,
                         SelectShared &sh, int tid, int &nA, int &nB)
 {
     constexpr int V = 16;
@@ -468,20 +485,6 @@ __device__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *c
         sh.nB = 0u;
     }
     __syncthreads();
-    // Loads stay inside the workspace row: base is a multiple of 16 below
-    // len <= clen, and clen is a multiple of 256.
-    auto load = [&](float (&v)[V], int64_t base) {
-        if (base < r.len) {
-#pragma unroll
-            for (int i = 0; i < V; i += 4) {
-                const float4 x = *(const float4 *)(r.src + base + i);
-                v[i] = x.x;
-                v[i + 1] = x.y;
-                v[i + 2] = x.z;
-                v[i + 3] = x.w;
-            }
-        }
-    };
     auto process = [&](const float (&v)[V], int64_t base) {
         uint32_t cls = 0, cnt = 0;
 #pragma unroll
@@ -518,15 +521,19 @@ __device__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *c
             }
         }
     };
-    float cur[V], nxt[V];
+    float cur[V], nx1[V], nx2[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) cur[i] = nxt[i] = 0.0f;
-    load(cur, (int64_t)tid * V);
+    for (int i = 0; i < V; ++i) cur[i] = nx1[i] = nx2[i] = 0.0f;
+    load16(r.src, r.len, (int64_t)tid * V, cur);
+    load16(r.src, r.len, ROUND + (int64_t)tid * V, nx1);
     for (int64_t e0 = 0; e0 < r.len; e0 += ROUND) {
-        load(nxt, e0 + ROUND + (int64_t)tid * V);
+        load16(r.src, r.len, e0 + 2 * ROUND + (int64_t)tid * V, nx2);
         process(cur, e0 + (int64_t)tid * V);
 #pragma unroll
-        for (int i = 0; i < V; ++i) cur[i] = nxt[i];
+        for (int i = 0; i < V; ++i) {
+            cur[i] = nx1[i];
+            nx1[i] = nx2[i];
+        }
     }
     __syncthreads();
     nA = (int)min(sh.nA, (uint32_t)kCapA);
@@ -538,7 +545,7 @@ __device__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *c
 // by its next 8 bits: a histogram over the chunk keys in the bin that beat
 // the floor gives the sub-bin holding the need-th best of them.  Narrows
 // [lo_u, hi_u) to it and returns the keys above it inside the old bin.
-__device__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, uint32_t &hi_u, int shift,
+__device__ __forceinline__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, uint32_t &hi_u, int shift,
                                uint32_t need, uint32_t *hist, SelectShared &sh, int tid)
 {
     const int lane = tid & 63;
@@ -547,16 +554,24 @@ __device__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, uint32_t &hi_u, 
     const float f_lo = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
     const float f_hi = score_of_orderable(hi_u);
     const bool top = hi_u == 0u;  // the bin reaches the top of the orderable range
-    for (int64_t e0 = 0; e0 < r.len; e0 += NT) {
-        const int64_t e = e0 + tid;
-        bool in = false;
-        uint32_t d = 0;
-        if (e < r.len) {
-            const float x = r.src[e];
-            in = (!r.filt || x > r.f_floor) && x >= f_lo && (top || !(x >= f_hi));
-            d = (orderable(x) >> (shift - 8)) & 255u;
+    constexpr int V = 16;
+    constexpr int ROUND = NT * V;
+    float cur[V], nxt[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) cur[i] = nxt[i] = 0.0f;
+    load16(r.src, r.len, (int64_t)tid * V, cur);
+    for (int64_t e0 = 0; e0 < r.len; e0 += ROUND) {
+        load16(r.src, r.len, e0 + ROUND + (int64_t)tid * V, nxt);
+        const int64_t base = e0 + (int64_t)tid * V;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const float x = cur[i];
+            const bool in = base + i < r.len && (!r.filt || x > r.f_floor) && x >= f_lo &&
+                            (top || !(x >= f_hi));
+            hist_add(hist, in, (orderable(x) >> (shift - 8)) & 255u, lane);
         }
-        hist_add(hist, in, d, lane);
+#pragma unroll
+        for (int i = 0; i < V; ++i) cur[i] = nxt[i];
     }
     __syncthreads();
     find_digit(hist, need, sh, tid);
@@ -615,7 +630,7 @@ __device__ int collect_pieces(uint64_t *cand, const RowCtx &r, int k, uint32_t *
     return cnt;
 }
 
-__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a)
+__global__ __launch_bounds__(NT, 4) void select_kernel(SelectArgs a)
 {
     extern __shared__ uint64_t smem[];
     __shared__ SelectShared sh;

@@ -587,7 +587,7 @@ __device__ __forceinline__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, 
 // is read in pieces, keys that cannot enter the current best k are dropped,
 // and the candidates are cut back to k by radix select whenever they exceed k.
 // Leaves them, unsorted, in cand[0..count) and returns the count.
-__device__ int collect_pieces(uint64_t *cand, const RowCtx &r, int k, uint32_t *hist,
+__device__ __noinline__ int collect_pieces(uint64_t *cand, const RowCtx r, int k, uint32_t *hist,
                               SelectShared &sh, int tid)
 {
     const int lane = tid & 63;

@@ -75,7 +75,7 @@ extern "C" {
 
 /* Supported ranges of this build. */
 #define CSA_MAX_HEADS 64
-#define CSA_MAX_K 2048
+#define CSA_MAX_K 4096
 
 /*
  * Tuning options; a zero field (or a NULL pointer to the struct) means

@@ -168,7 +168,7 @@ const char *csa_status_str(int status)
     case CSA_ERR_BAD_DTYPE: return "bad dtype: expected CSA_F32 or CSA_BF16";
     case CSA_ERR_MISALIGNED: return "misaligned pointer";
     case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small for one query block";
-    case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 2048 or T >= 2^31)";
+    case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 4096 or T >= 2^31)";
     case CSA_ERR_HIP: return "HIP call or kernel launch failed";
     case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256, key_tile one of 64/128/256, reserved fields 0";
     default: return "unknown status";

@@ -32,14 +32,23 @@ namespace {
 
 constexpr int NT = kSelectThreads;
 constexpr int NWAVES = NT / 64;
-constexpr int kCapA = 2048;           // keys above the boundary bin (< k <= 2048)
-constexpr int kCapB = 2048;           // keys in the boundary bin
-constexpr int kCand = kCapA + kCapB;  // 64-bit key slots in LDS
-constexpr int kBuckets = 1536;        // bucket sort: one 32-bit word per bucket
 constexpr int kSortMaxBucket = 64;    // larger buckets: bitonic sort instead
-constexpr int PER_MAX = kCand / NT;   // keys per thread in the sort and radix select
-static_assert(kSelectPiece + 2048 <= kCand, "fallback pieces must fit beside k keys");
-static_assert(kBuckets % NT == 0 && kBuckets >= 256, "bucket words double as a 256-bin histogram");
+
+// Capacities of the kernel for k <= K (K = 2048 or 4096).  Region A holds
+// the keys above the boundary bin (fewer than k), region B the keys in it
+// (the running list, up to k keys, also goes there after the sort).
+template <int K>
+struct Caps {
+    static constexpr int A = K;
+    static constexpr int B = K;
+    static constexpr int Cand = A + B;        // 64-bit key slots in LDS
+    static constexpr int Buckets = Cand * 3 / 8;  // bucket sort: one 32-bit word per bucket
+    static constexpr int PER = Cand / NT;     // keys per thread in the sort and radix select
+    static constexpr int PT = K / NT;         // merged outputs per thread
+    static_assert(kSelectPiece + K <= Cand, "fallback pieces must fit beside k keys");
+    static_assert(Buckets % NT == 0 && Buckets >= 256, "bucket words double as a 256-bin histogram");
+    static constexpr size_t lds_bytes = (size_t)Cand * 8 + (size_t)Buckets * 4;
+};
 
 __device__ inline float key_score(uint64_t key)
 {
@@ -204,13 +213,15 @@ __device__ inline void find_digit(const uint32_t *hist, uint32_t need, SelectSha
     }
 }
 
-// Keeps the k largest of cand[0..cnt) (k < cnt <= kCand) in cand[0..k), any
+// Keeps the k largest of cand[0..cnt) (k < cnt <= Caps<K>::Cand) in cand[0..k), any
 // order.  All entries must agree on the key bits above `first_shift + 8`;
 // digits are 8 bits wide from there down (the last one clamped at bit 0).
 // hist has 256 words.
+template <int K>
 __device__ void radix_select(uint64_t *cand, int cnt, int k, uint32_t *hist, SelectShared &sh,
                              int tid, int first_shift = 56)
 {
+    constexpr int PER_MAX = Caps<K>::PER;
     const int lane = tid & 63;
     uint32_t need = (uint32_t)k;
     uint64_t prefix = 0, mask = 0;
@@ -259,7 +270,7 @@ __device__ void radix_select(uint64_t *cand, int cnt, int k, uint32_t *hist, Sel
     __syncthreads();
 }
 
-// Sorts cand[0..n) descending; n <= kCand, and the buffer holds the next
+// Sorts cand[0..n) descending; n <= the buffer size, which holds the next
 // power of two.  Used for degenerate inputs (huge runs of equal scores).
 __device__ void bitonic_desc(uint64_t *cand, int n, int tid)
 {
@@ -284,27 +295,32 @@ __device__ void bitonic_desc(uint64_t *cand, int n, int tid)
     }
 }
 
-// Sorts the nA keys at cand[0..nA) and the nB keys at cand[kCapA..kCapA+nB)
+// Sorts the nA keys at cand[0..nA) and the nB keys at cand[A..A+nB)
 // together, descending, into cand[0..nA+nB).  Every A key must be larger
 // than every B key (A = above the boundary, B = in it; either may be empty).
 //
 // Bucket sort with the keys held in registers: each region's score range
 // [min, max] is cut into buckets of equal width in score value (B gets a
-// share of the kBuckets buckets proportional to its size, A the rest), which
+// share of the buckets proportional to its size, A the rest), which
 // is monotone, so bucket order is key order.  One LDS atomic per key counts
 // its bucket and gives its slot there; a prefix sum over the buckets (from the
 // top) gives each bucket's first position; keys are scattered into bucket
 // order, and each then finds its place inside its bucket by counting the
 // larger keys there.  If a bucket holds more than kSortMaxBucket keys (many
 // equal or clustered scores) a bitonic sort of the whole buffer takes over.
-// bk: kBuckets words.
+// bk: Caps<K>::Buckets words.
+template <int K>
 __device__ __forceinline__ void sort_keys(uint64_t *cand, int nA, int nB, uint32_t *bk, SelectShared &sh,
                           int tid)
 {
+    constexpr int kCapA = Caps<K>::A;
+    constexpr int kCand = Caps<K>::Cand;
+    constexpr int kBuckets = Caps<K>::Buckets;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    constexpr int PT = PER_MAX;  // slots 0..PT/2-1 from A's region, the rest from B's
+    constexpr int PT = Caps<K>::PER;  // slots 0..PT/2-1 from A's region, the rest from B's
     constexpr int PH = PT / 2;
+    static_assert(Caps<K>::A == Caps<K>::B, "equal regions: half the slots each");
     uint64_t key[PT];
     uint32_t loA = 0xFFFFFFFFu, hiA = 0u, loB = 0xFFFFFFFFu, hiB = 0u;
 #pragma unroll
@@ -469,14 +485,17 @@ __device__ inline void load16(const float *src, int64_t len, int64_t base, float
 // One streaming pass over the row's chunk scores, 16 consecutive keys per
 // thread per round, the next two rounds' loads in flight while this round is
 // classified.  A key beating the floor goes to region A (cand[0..)) if its
-// score is >= f_sure, to region B (cand[kCapA..)) if it is >= f_edge, else it
+// score is >= f_sure, to region B (cand[A..)) if it is >= f_edge, else it
 // is dropped.  Each wave reserves its slots with one LDS atomic per region
 // per round; the order inside a region is arbitrary (the sort fixes it).
 // Returns the region sizes (clamped to the capacities, which the callers'
 // counts never exceed).
+template <int K>
 __device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *cand,
                         SelectShared &sh, int tid, int &nA, int &nB)
 {
+    constexpr int kCapA = Caps<K>::A;
+    constexpr int kCapB = Caps<K>::B;
     constexpr int V = 16;
     constexpr int ROUND = NT * V;
     const int lane = tid & 63;
@@ -587,6 +606,7 @@ __device__ __forceinline__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, 
 // is read in pieces, keys that cannot enter the current best k are dropped,
 // and the candidates are cut back to k by radix select whenever they exceed k.
 // Leaves them, unsorted, in cand[0..count) and returns the count.
+template <int K>
 __device__ __noinline__ int collect_pieces(uint64_t *cand, const RowCtx r, int k, uint32_t *hist,
                               SelectShared &sh, int tid)
 {
@@ -618,7 +638,7 @@ __device__ __noinline__ int collect_pieces(uint64_t *cand, const RowCtx r, int k
         __syncthreads();
         cnt += (int)sh.count;
         if (cnt > k) {
-            radix_select(cand, cnt, k, hist, sh, tid);
+            radix_select<K>(cand, cnt, k, hist, sh, tid);
             cnt = k;
         }
         if (cnt >= k) {
@@ -630,13 +650,16 @@ __device__ __noinline__ int collect_pieces(uint64_t *cand, const RowCtx r, int k
     return cnt;
 }
 
-__global__ __launch_bounds__(NT, 4) void select_kernel(SelectArgs a)
+template <int K>
+__global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArgs a)
 {
+    constexpr int kCapA = Caps<K>::A;
+    constexpr int kCapB = Caps<K>::B;
     extern __shared__ uint64_t smem[];
     __shared__ SelectShared sh;
     const int k = (int)a.k;
-    uint64_t *cand = smem;                        // kCand keys
-    uint32_t *bk = (uint32_t *)(smem + kCand);    // kBuckets words (also a 256-bin histogram)
+    uint64_t *cand = smem;                                 // Caps<K>::Cand keys
+    uint32_t *bk = (uint32_t *)(smem + Caps<K>::Cand);    // bucket words (also a 256-bin histogram)
     const int tid = threadIdx.x;
     const int64_t rl = a.rows - 1 - (int64_t)blockIdx.x;  // long rows first
     const int64_t row = a.row0 + rl;
@@ -672,7 +695,7 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(SelectArgs a)
             const ChunkMeta mt = a.meta[rl];
             if (mt.total <= (uint32_t)k) {
                 // Every key that beats the floor (at most k of them).
-                collect(r, -__builtin_inff(), __builtin_inff(), cand, sh, tid, nA, nB);
+                collect<K>(r, -__builtin_inff(), __builtin_inff(), cand, sh, tid, nA, nB);
                 done = true;
             } else {
                 constexpr int BIN_SHIFT = 32 - kHistBits;  // orderable bits below the bin
@@ -692,17 +715,17 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(SelectArgs a)
                     // bin 0 starts at -inf, the top bin has no upper edge).
                     const float f_sure = hi_u == 0u ? __builtin_nanf("") : score_of_orderable(hi_u);
                     const float f_edge = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
-                    collect(r, f_sure, f_edge, cand, sh, tid, nA, nB);
+                    collect<K>(r, f_sure, f_edge, cand, sh, tid, nA, nB);
                     done = true;
                 }
             }
         }
         if (!done) {
             // No summary (fp32 scores) or massively tied scores.
-            nA = collect_pieces(cand, r, k, bk, sh, tid);
+            nA = collect_pieces<K>(cand, r, k, bk, sh, tid);
             nB = 0;
         }
-        if (nA + nB > 1) sort_keys(cand, nA, nB, bk, sh, tid);
+        if (nA + nB > 1) sort_keys<K>(cand, nA, nB, bk, sh, tid);
         cnt_q = min(k, nA + nB);
     }
 
@@ -717,7 +740,7 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(SelectArgs a)
     // Merge with the running list (both sorted descending) and keep the
     // first min(k, |L| + |Q|) entries: merge-path split, 8 outputs per thread.
     const int total = min(k, cnt_l + cnt_q);
-    constexpr int PT = (2048 + NT - 1) / NT;  // outputs per thread (k <= 2048)
+    constexpr int PT = Caps<K>::PT;  // outputs per thread (k <= K)
     const int p0 = tid * PT;
     uint64_t outv[PT];
     uint64_t kth = 0;  // the entry at position k-1, for the next chunk's floor
@@ -770,7 +793,7 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(SelectArgs a)
                 }
             }
         }
-        // NT*PT >= k (k <= CSA_MAX_K = 2048), so every position is written.
+        // NT*PT = K >= k, so every position is written.
     } else {
         uint64_t *dst = a.lists + rl * a.k;
         if ((k & 1) == 0 && p0 + PT <= total) {  // 16-byte aligned, whole
@@ -799,8 +822,19 @@ __global__ __launch_bounds__(NT, 4) void select_kernel(SelectArgs a)
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0) return hipSuccess;
-    const size_t lds = (size_t)kCand * sizeof(uint64_t) + (size_t)kBuckets * sizeof(uint32_t);
-    select_kernel<<<dim3((unsigned)a.rows), dim3(NT), lds, stream>>>(a);
+    if (a.k <= 2048) {
+        select_kernel<2048><<<dim3((unsigned)a.rows), dim3(NT), Caps<2048>::lds_bytes, stream>>>(a);
+    } else {
+        static bool attr_set = false;  // benign race: every caller sets the same value
+        if (!attr_set) {
+            const hipError_t e = hipFuncSetAttribute((const void *)select_kernel<4096>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)Caps<4096>::lds_bytes);
+            if (e != hipSuccess) return e;
+            attr_set = true;
+        }
+        select_kernel<4096><<<dim3((unsigned)a.rows), dim3(NT), Caps<4096>::lds_bytes, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

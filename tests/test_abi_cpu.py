@@ -89,7 +89,7 @@ def _call(lib, q=1, w=1, kc=1, dtype=1, S=8, T=8, H=4, D=32, m=4, k=2, q_pos0=0,
     (dict(m=0), 2),
     (dict(k=0), 2),
     (dict(q_pos0=-3), 2),
-    (dict(k=4096), 6),
+    (dict(k=4097), 6),
     (dict(q=0), 1),
     (dict(w=0), 1),
     (dict(idx=0), 1),

@@ -178,6 +178,47 @@ def test_chunk_and_tile_grid_bit_identical():
             assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
 
 
+def test_large_k_integer_bit_exact():
+    """k up to 4096 (the larger select configuration): integer inputs bit for
+    bit, with one chunk and with chunks much shorter than k (the running list
+    holds more keys than a chunk has)."""
+    S, T, H, D, m, k = 2048, 6000, 64, 128, 1, 4096
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=21, dtype=torch.bfloat16, signed_w=True)
+    q_pos0 = 3000  # rows see 3001..5048 keys: below, at and above k
+    say("large k integer S=%d T=%d k=%d" % (S, T, k))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    for chunk in (0, 1024, 2560):
+        say("  chunk=%d" % chunk)
+        g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, chunk_keys=chunk)
+        assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
+@pytest.mark.parametrize("k", [2049, 3000, 4096])
+def test_large_k_bf16_gaussian(k):
+    S, T, H, D, m = 4096, 6144, 64, 128, 1
+    q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=22)
+    q_pos0 = 2048  # rows see 2049..6144 keys
+    say("large k bf16 S=%d T=%d k=%d" % (S, T, k))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    edge = np.array([k - q_pos0 - 2, k - q_pos0 - 1, k - q_pos0, S - 1])  # n(row) around k
+    rows = np.unique(np.concatenate([np.arange(0, S, 16), np.clip(edge, 0, S - 1)]))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, rows=rows, q_pos0=q_pos0)
+    fails, stats = checks.check_float(g_idx[rows], g_sc[rows], o_idx, o_sc,
+                                      q.float().numpy()[rows], w.float().numpy()[rows],
+                                      kc.float().numpy(), rows + q_pos0, T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
+def test_large_k_beyond_keys_pads():
+    S, T, H, D, m, k = 64, 1000, 8, 64, 1, 4096
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=23, dtype=torch.bfloat16, signed_w=True)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=900)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=900)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+    assert (g_idx[:, 1000:] == -1).all()
+
+
 def test_small_workspace_many_passes():
     S, T, H, D, m, k = 2000, 500, 8, 64, 4, 64
     q, w, kc = inputs.integer_valued(S, T, H, D, seed=6, dtype=torch.bfloat16, signed_w=True)

@@ -138,6 +138,26 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
                      void *stream);
 
 /*
+ * Batched form (B=1 is the single call above): B independent problems of the
+ * same shape, each with its own queries and its own compressed keys, e.g. the
+ * sequences of a batch.  Layouts are the single call's with a leading batch
+ * dimension, densely packed:
+ *   q [B][S][H_I][D_I], w [B][S][H_I], kc [B][T][D_I], idx/score [B][S][k].
+ * Problem b is exactly csa_indexer_topk on the b-th slices (same q_pos0 and
+ * options), so its outputs are bit-identical to that call's.  The workspace
+ * is sized for one problem (csa_indexer_topk_workspace_size with the same
+ * S, T, ...) and is reused by the problems in turn, all enqueued on `stream`.
+ * B = 0 is valid (no work); B < 0 is CSA_ERR_BAD_SHAPE.  All argument checks
+ * run before any HIP call; a HIP failure while enqueueing problem b returns
+ * CSA_ERR_HIP with problems 0..b-1 already enqueued.
+ */
+int csa_indexer_topk_batched(const void *q, const void *w, const void *kc, int32_t dtype,
+                             int64_t B, int64_t S, int64_t T, int32_t H_I, int32_t D_I,
+                             int32_t m, int64_t k, int64_t q_pos0, int32_t *idx, float *score,
+                             void *workspace, size_t workspace_bytes, const csa_opts *opts,
+                             void *stream);
+
+/*
  * Kernel timing for benchmarks.  While enabled, every kernel launch made by
  * csa_indexer_topk on this process is bracketed by HIP events recorded on the
  * launch's stream.  csa_profile_collect waits for those events, adds up the

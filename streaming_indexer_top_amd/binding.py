@@ -24,7 +24,8 @@ CSA_KERNEL_KINDS = 2
 KERNEL_NAMES = ("score", "select")
 
 EXPORTS = ("csa_abi_version", "csa_status_str", "csa_indexer_topk_workspace_size",
-           "csa_indexer_topk", "csa_profile_enable", "csa_profile_collect")
+           "csa_indexer_topk", "csa_indexer_topk_batched", "csa_profile_enable",
+           "csa_profile_collect")
 
 
 class CsaError(RuntimeError):
@@ -71,6 +72,10 @@ def load_library(path: str | None = None):
     lib.csa_indexer_topk.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i64, i64,
                                      vp, vp, vp, ctypes.c_size_t, ctypes.POINTER(csa_opts), vp]
     lib.csa_indexer_topk.restype = ctypes.c_int
+    lib.csa_indexer_topk_batched.argtypes = [vp, vp, vp, i32, i64, i64, i64, i32, i32, i32, i64,
+                                             i64, vp, vp, vp, ctypes.c_size_t,
+                                             ctypes.POINTER(csa_opts), vp]
+    lib.csa_indexer_topk_batched.restype = ctypes.c_int
     lib.csa_profile_enable.argtypes = [ctypes.c_int]
     lib.csa_profile_enable.restype = ctypes.c_int
     lib.csa_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -126,14 +131,30 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
     or all float32.  Returns (idx [S, k] int32, score [S, k] float32), rows
     ordered by score descending then key index ascending, padded with -1 /
     -inf.  Runs on torch's current stream; does not synchronise.
+
+    Batched form: q [B, S, H, D], w [B, S, H], kc [B, T, D] (B independent
+    problems, each with its own keys) gives idx, score [B, S, k]; the
+    workspace is sized for one problem and reused.
     """
-    if q.dim() != 3 or w.dim() != 2 or kc.dim() != 2:
-        raise ValueError("q must be [S,H,D], w [S,H], kc [T,D]")
-    S, H, D = q.shape
-    T = kc.shape[0]
-    if tuple(w.shape) != (S, H) or (kc.shape[1] != D):
-        raise ValueError("shape mismatch: q %s, w %s, kc %s" % (tuple(q.shape), tuple(w.shape),
-                                                               tuple(kc.shape)))
+    batched = q.dim() == 4
+    if batched:
+        if w.dim() != 3 or kc.dim() != 3:
+            raise ValueError("batched: q must be [B,S,H,D], w [B,S,H], kc [B,T,D]")
+        B, S, H, D = q.shape
+        T = kc.shape[1]
+        if tuple(w.shape) != (B, S, H) or kc.shape[0] != B or kc.shape[2] != D:
+            raise ValueError("shape mismatch: q %s, w %s, kc %s"
+                             % (tuple(q.shape), tuple(w.shape), tuple(kc.shape)))
+        oshape = (B, S, k)
+    else:
+        if q.dim() != 3 or w.dim() != 2 or kc.dim() != 2:
+            raise ValueError("q must be [S,H,D], w [S,H], kc [T,D]")
+        S, H, D = q.shape
+        T = kc.shape[0]
+        if tuple(w.shape) != (S, H) or (kc.shape[1] != D):
+            raise ValueError("shape mismatch: q %s, w %s, kc %s"
+                             % (tuple(q.shape), tuple(w.shape), tuple(kc.shape)))
+        oshape = (S, k)
     if not (q.dtype == w.dtype == kc.dtype):
         raise TypeError("q, w, kc must share one dtype")
     dev = q.device
@@ -146,14 +167,15 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
     lib = load_library()
     o = _opts(chunk_keys, key_tile, workspace_budget)
     if out is None:
-        idx = torch.empty((S, k), dtype=torch.int32, device=dev)
-        score = torch.empty((S, k), dtype=torch.float32, device=dev)
+        idx = torch.empty(oshape, dtype=torch.int32, device=dev)
+        score = torch.empty(oshape, dtype=torch.float32, device=dev)
     else:
         idx, score = out
-        if idx.shape != (S, k) or score.shape != (S, k) or idx.dtype != torch.int32 \
-                or score.dtype != torch.float32 or not idx.is_contiguous() \
-                or not score.is_contiguous():
-            raise ValueError("out must be contiguous int32/float32 tensors of shape [S, k]")
+        if tuple(idx.shape) != oshape or tuple(score.shape) != oshape \
+                or idx.dtype != torch.int32 or score.dtype != torch.float32 \
+                or not idx.is_contiguous() or not score.is_contiguous():
+            raise ValueError("out must be contiguous int32/float32 tensors of shape %s"
+                             % (oshape,))
     if workspace is None:
         nbytes = workspace_size(S, T, H, D, m, k, q_pos0=q_pos0, dtype=q.dtype,
                                 chunk_keys=chunk_keys, key_tile=key_tile,
@@ -163,12 +185,20 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
         nbytes = workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
-        _check(lib.csa_indexer_topk(
-            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(w.data_ptr()),
-            ctypes.c_void_p(kc.data_ptr()), dt, S, T, H, D, int(m), int(k), int(q_pos0),
-            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(score.data_ptr()),
-            ctypes.c_void_p(workspace.data_ptr()), nbytes, ctypes.byref(o),
-            ctypes.c_void_p(stream)))
+        if batched:
+            _check(lib.csa_indexer_topk_batched(
+                ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                ctypes.c_void_p(kc.data_ptr()), dt, B, S, T, H, D, int(m), int(k), int(q_pos0),
+                ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(score.data_ptr()),
+                ctypes.c_void_p(workspace.data_ptr()), nbytes, ctypes.byref(o),
+                ctypes.c_void_p(stream)))
+        else:
+            _check(lib.csa_indexer_topk(
+                ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+                ctypes.c_void_p(kc.data_ptr()), dt, S, T, H, D, int(m), int(k), int(q_pos0),
+                ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(score.data_ptr()),
+                ctypes.c_void_p(workspace.data_ptr()), nbytes, ctypes.byref(o),
+                ctypes.c_void_p(stream)))
     return idx, score
 
 

@@ -191,15 +191,23 @@ int csa_indexer_topk_workspace_size(int64_t S, int64_t T, int32_t H_I, int32_t D
     return CSA_OK;
 }
 
-int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype, int64_t S,
-                     int64_t T, int32_t H_I, int32_t D_I, int32_t m, int64_t k, int64_t q_pos0,
-                     int32_t *idx, float *score, void *workspace, size_t workspace_bytes,
-                     const csa_opts *opts, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Argument checks of one problem, before any HIP call; on success *rows_out
+// is the pass size the workspace allows.
+int check_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_t S, int64_t T,
+               int32_t H_I, int32_t D_I, int32_t m, int64_t k, int64_t q_pos0, int32_t *idx,
+               float *score, void *workspace, size_t workspace_bytes, const csa_opts *opts,
+               Plan *plan_out, int64_t *rows_out)
 {
     int st = check_args(S, T, H_I, D_I, m, k, q_pos0, dtype, opts);
     if (st != CSA_OK) return st;
-    if (S == 0) return CSA_OK;
     const Plan p = make_plan(S, T, m, q_pos0, opts);
+    *plan_out = p;
+    *rows_out = 0;
+    if (S == 0) return CSA_OK;
     if (!q || !w || !idx || !score) return CSA_ERR_NULL_PTR;
     if (p.n_max > 0 && !kc) return CSA_ERR_NULL_PTR;
     const size_t esz = dtype == CSA_BF16 ? 2 : 4;
@@ -211,6 +219,19 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
         if (!workspace) return CSA_ERR_NULL_PTR;
         rows = rows_fitting(p, S, k, workspace_bytes);
         if (rows <= 0) return CSA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    *rows_out = rows;
+    return CSA_OK;
+}
+
+// One problem, its arguments already checked: the pass plan and the launches.
+int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_t S, int64_t T,
+             int32_t H_I, int32_t D_I, int32_t m, int64_t k, int64_t q_pos0, int32_t *idx,
+             float *score, void *workspace, const Plan &p, int64_t rows, void *stream)
+{
+    int st = CSA_OK;
+    if (S == 0) return CSA_OK;
+    if (p.chunk > 0) {
         if (rows < S) {
             // Several passes.  Score workgroups of one pass run in rounds of
             // (CUs x workgroups per CU); a partial round leaves CUs idle for
@@ -293,6 +314,53 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
             st = launch_timed(CSA_KERNEL_SELECT, s, [&] { return csa::launch_select(se, s); });
             if (st != CSA_OK) return st;
         }
+    }
+    return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype, int64_t S,
+                     int64_t T, int32_t H_I, int32_t D_I, int32_t m, int64_t k, int64_t q_pos0,
+                     int32_t *idx, float *score, void *workspace, size_t workspace_bytes,
+                     const csa_opts *opts, void *stream)
+{
+    Plan p;
+    int64_t rows = 0;
+    const int st = check_call(q, w, kc, dtype, S, T, H_I, D_I, m, k, q_pos0, idx, score,
+                              workspace, workspace_bytes, opts, &p, &rows);
+    if (st != CSA_OK) return st;
+    return run_call(q, w, kc, dtype, S, T, H_I, D_I, m, k, q_pos0, idx, score, workspace, p, rows,
+                    stream);
+}
+
+int csa_indexer_topk_batched(const void *q, const void *w, const void *kc, int32_t dtype,
+                             int64_t B, int64_t S, int64_t T, int32_t H_I, int32_t D_I,
+                             int32_t m, int64_t k, int64_t q_pos0, int32_t *idx, float *score,
+                             void *workspace, size_t workspace_bytes, const csa_opts *opts,
+                             void *stream)
+{
+    if (B < 0) return CSA_ERR_BAD_SHAPE;
+    Plan p;
+    int64_t rows = 0;
+    // Every problem has the same shape, so one check covers them all (slice
+    // offsets keep the alignments: H_I*D_I and D_I elements are multiples of
+    // 16 bytes, S*k outputs of 4).
+    const int st = check_call(q, w, kc, dtype, S, T, H_I, D_I, m, k, q_pos0, idx, score,
+                              workspace, workspace_bytes, opts, &p, &rows);
+    if (st != CSA_OK || B == 0 || S == 0) return st;
+    const size_t esz = dtype == CSA_BF16 ? 2 : 4;
+    for (int64_t b = 0; b < B; ++b) {
+        // The problems share the workspace: their launches are ordered on
+        // the one stream.
+        const int sb = run_call((const char *)q + (size_t)b * S * H_I * D_I * esz,
+                                (const char *)w + (size_t)b * S * H_I * esz,
+                                kc ? (const char *)kc + (size_t)b * T * D_I * esz : nullptr, dtype,
+                                S, T, H_I, D_I, m, k, q_pos0, idx + (size_t)b * S * k,
+                                score + (size_t)b * S * k, workspace, p, rows, stream);
+        if (sb != CSA_OK) return sb;
     }
     return CSA_OK;
 }

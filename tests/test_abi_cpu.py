@@ -105,6 +105,23 @@ def test_argument_checks_fail_before_any_device_work(kw, status):
     assert _call(lib, **kw) == status
 
 
+def _call_batched(lib, B=2, q=1, ws=None, ws_bytes=0, S=8, T=8, k=2):
+    P = ctypes.c_void_p
+    al = 4096
+    conv = lambda v: P(al * v if isinstance(v, int) and v in (0, 1) else v)
+    return lib.csa_indexer_topk_batched(conv(q), conv(1), conv(1), 1, B, S, T, 4, 32, 4, k, 0,
+                                        conv(1), conv(1), P(ws), ws_bytes, None, None)
+
+
+def test_batched_argument_checks():
+    lib = csa.load_library()
+    assert _call_batched(lib, B=-1) == 2
+    assert _call_batched(lib, B=3, q=0) == 1
+    assert _call_batched(lib, B=3, k=5000) == 6
+    assert _call_batched(lib, B=3) == 1  # keys exist, so a workspace is required
+    assert _call_batched(lib, B=0, S=0) == 0  # no problem: nothing to do
+
+
 def test_workspace_too_small():
     lib = csa.load_library()
     assert _call(lib, ws=4096 * 16, ws_bytes=64, S=4096, T=1024) == 5

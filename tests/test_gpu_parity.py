@@ -219,6 +219,42 @@ def test_large_k_beyond_keys_pads():
     assert (g_idx[:, 1000:] == -1).all()
 
 
+def _stack(problems):
+    return [torch.stack([p[i] for p in problems]).contiguous() for i in range(3)]
+
+
+def test_batched_integer_bit_exact():
+    """B problems with their own keys: each batch equals the oracle bit for
+    bit, and equals the single call on its slices."""
+    B, S, T, H, D, m, k = 3, 1500, 400, 64, 128, 4, 64
+    probs = [inputs.integer_valued(S, T, H, D, seed=30 + b, dtype=torch.bfloat16, signed_w=True)
+             for b in range(B)]
+    q, w, kc = _stack(probs)
+    say("batched integer B=%d S=%d T=%d k=%d" % (B, S, T, k))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k)
+    assert g_idx.shape == (B, S, k)
+    for b in range(B):
+        o_idx, o_sc = oracle_topk(*probs[b], m, k)
+        assert_no_fail(checks.check_exact(g_idx[b], g_sc[b], o_idx, o_sc))
+        s_idx, s_sc = gpu_topk(*probs[b], m, k)
+        assert np.array_equal(s_idx, g_idx[b])
+        assert np.array_equal(s_sc.view(np.uint32), g_sc[b].view(np.uint32))
+
+
+def test_batched_bf16_matches_single_calls_multi_pass():
+    B, S, T, H, D, m, k = 2, 3000, 750, 64, 128, 4, 128
+    probs = [inputs.bf16_gaussian(S, T, H, D, seed=40 + b) for b in range(B)]
+    q, w, kc = _stack(probs)
+    for budget, chunk in ((0, 0), (1, 256)):  # one pass; many passes and chunks
+        say("batched bf16 budget=%d chunk=%d" % (budget, chunk))
+        g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=100, workspace_budget=budget,
+                               chunk_keys=chunk)
+        for b in range(B):
+            s_idx, s_sc = gpu_topk(*probs[b], m, k, q_pos0=100)
+            assert np.array_equal(s_idx, g_idx[b])
+            assert np.array_equal(s_sc.view(np.uint32), g_sc[b].view(np.uint32))
+
+
 def test_small_workspace_many_passes():
     S, T, H, D, m, k = 2000, 500, 8, 64, 4, 64
     q, w, kc = inputs.integer_valued(S, T, H, D, seed=6, dtype=torch.bfloat16, signed_w=True)

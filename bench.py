@@ -221,6 +221,86 @@ def run_sweep(args, q, w, kc, c, dev, base_alloc):
         del idx, score
 
 
+def run_batched(args, dev):
+    """B independent problems of the workload's shape (own seeded inputs each)
+    in one batched call; one JSON line with the batch's pairs/s."""
+    c = inputs.config(args.workload)
+    S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    B = args.batch
+    probs = [inputs.bf16_gaussian(S, T, H, D, seed=100 * args.workload + b, device=dev)
+             for b in range(B)]
+    q, w, kc = [torch.stack([p[i] for p in probs]).contiguous() for i in range(3)]
+    del probs
+    idx = torch.empty((B, S, k), dtype=torch.int32, device=dev)
+    score = torch.empty((B, S, k), dtype=torch.float32, device=dev)
+    ws_bytes = csa.workspace_size(S, T, H, D, m, k, chunk_keys=args.chunk, key_tile=args.tile,
+                                  workspace_budget=args.budget)
+    workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    kw = dict(chunk_keys=args.chunk, key_tile=args.tile, workspace_budget=args.budget,
+              workspace=workspace, out=(idx, score))
+    for _ in range(args.warmup):
+        csa.topk(q, w, kc, m, k, **kw)
+    torch.cuda.synchronize()
+    csa.profile_collect()
+    csa.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        csa.topk(q, w, kc, m, k, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    csa.profile_enable(False)
+    prof = csa.profile_collect()
+    ms = (t1 - t0) * 1e3 / args.steps
+    P = B * pair_count(S, T, m)
+    print(json.dumps({
+        "mode": "batched", "batch": B, "workload": args.workload, "S": S, "T": T, "k": k,
+        "ms_per_call": ms, "pairs_per_s": P / (ms * 1e-3),
+        "mfma_util_pct": 100.0 * P * 2 * H * D / (ms * 1e-3) / (MFMA_BUSY_PEAK * 1e12),
+        "score_ms": prof["score"][0] / args.steps, "select_ms": prof["select"][0] / args.steps,
+        "score_launches": prof["score"][1] / args.steps, "workspace_bytes": ws_bytes}),
+        flush=True)
+
+
+def run_decode(args, dev):
+    """R new queries at the end of the workload's sequence (q_pos0 = m*T - R,
+    every query sees all T keys): the automatic plan (key splits) and the
+    chunked plan (key_splits=1), one JSON line each."""
+    c = inputs.config(args.workload)
+    _, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
+    R = args.decode
+    q, w, kc = inputs.bf16_gaussian(R, T, H, D, seed=1000 + args.workload, device=dev)
+    q_pos0 = m * T - R
+    P = pair_count(R, T, m, q_pos0)
+    ref = None
+    for splits in (0, 1):
+        kw = dict(q_pos0=q_pos0, key_splits=splits)
+        for _ in range(args.warmup):
+            csa.topk(q, w, kc, m, k, **kw)
+        torch.cuda.synchronize()
+        csa.profile_collect()
+        csa.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            out = csa.topk(q, w, kc, m, k, **kw)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        csa.profile_enable(False)
+        prof = csa.profile_collect()
+        if ref is None:
+            ref = out
+        same = bool(torch.equal(ref[0], out[0])) and bool(
+            torch.equal(ref[1].view(torch.int32), out[1].view(torch.int32)))
+        ms = (t1 - t0) * 1e3 / args.steps
+        print(json.dumps({
+            "mode": "decode", "plan": "key splits (auto)" if splits == 0 else "chunks only",
+            "rows": R, "T": T, "k": k, "q_pos0": q_pos0, "ms_per_call": ms,
+            "pairs_per_s": P / (ms * 1e-3),
+            "mfma_util_pct": 100.0 * P * 2 * H * D / (ms * 1e-3) / (MFMA_BUSY_PEAK * 1e12),
+            "kernel_ms": {kk: v[0] / args.steps for kk, v in prof.items()},
+            "launches": {kk: v[1] / args.steps for kk, v in prof.items()},
+            "bit_identical_to_auto": same}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +320,12 @@ def main():
     ap.add_argument("--sweep-chunks", default="4096,8192,16384,32768,65536")
     ap.add_argument("--sweep-tiles", default="64,128,256")
     ap.add_argument("--sweep-ks", default="", help="top-k values to sweep (default: the workload's k)")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="time this many new queries at the end of the workload's sequence "
+                         "(decode shape) with and without key splits")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="time one batched call over this many independent problems of the "
+                         "workload's shape (one JSON line)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device copy run once before timing, as a known "
                          "reference for HBM traffic counters")
@@ -265,6 +351,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     csa.load_library()
+    if args.batch:
+        run_batched(args, dev)
+        return
+    if args.decode:
+        run_decode(args, dev)
+        return
 
     torch.cuda.reset_peak_memory_stats(dev)
     base_alloc = torch.cuda.memory_allocated(dev)
@@ -360,7 +452,8 @@ def main():
             "flops_per_launch": flops_per_launch,
         },
         "mfma_util_pct": 100.0 * flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-        "kernel_ms_per_step": {"score": score_ms / args.steps, "select": sel_ms / args.steps},
+        "kernel_ms_per_step": {"score": score_ms / args.steps, "select": sel_ms / args.steps,
+                               "merge": prof["merge"][0] / args.steps},
         "peak_hbm_gb": peak / 1e9,
         "peak_hbm": {"total_gib": peak / 2 ** 30, "workspace_bytes": ws_bytes,
                      "resident_inputs_outputs_gib": resident / 2 ** 30,

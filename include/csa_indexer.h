@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 /* Status codes. */
 #define CSA_OK 0
@@ -88,7 +88,15 @@ typedef struct csa_opts {
     int64_t chunk_keys;
     /* Keys staged in LDS per step of the score kernel: 64, 128, 256, or 0. */
     int32_t key_tile;
-    int32_t reserved0; /* must be 0 */
+    /* Key splits (bf16 only, ignored when chunk_keys is set): the usable keys
+     * form one chunk cut into this many splits that are scored and selected
+     * in parallel, each split's best k going to its own list, and the lists
+     * are merged pairwise.  For problems with few query rows (decoding a few
+     * new queries against a long key cache), where chunks alone would leave
+     * most of the GPU idle.  0 = automatic (used for fewer than 2048 rows
+     * when one pass fits the workspace budget), 1 = never, or a power of two
+     * up to 64. */
+    int32_t key_splits;
     /* Upper bound, in bytes, on the workspace that
      * csa_indexer_topk_workspace_size plans for; 0 means 2 GiB.  A smaller
      * workspace only makes the library process fewer query rows per pass. */
@@ -168,7 +176,8 @@ int csa_indexer_topk_batched(const void *q, const void *w, const void *kc, int32
  */
 #define CSA_KERNEL_SCORE 0  /* chunk scoring: MFMA contraction + ReLU + head sum */
 #define CSA_KERNEL_SELECT 1 /* chunk top-k, merge into running lists, emit */
-#define CSA_KERNEL_KINDS 2
+#define CSA_KERNEL_MERGE 2  /* merge rounds of key-split lists, emit */
+#define CSA_KERNEL_KINDS 3
 int csa_profile_enable(int enable);
 int csa_profile_collect(double *ms_out, int64_t *launches_out, int32_t n_kinds);
 

@@ -20,8 +20,9 @@ CSA_F32 = 0
 CSA_BF16 = 1
 CSA_KERNEL_SCORE = 0
 CSA_KERNEL_SELECT = 1
-CSA_KERNEL_KINDS = 2
-KERNEL_NAMES = ("score", "select")
+CSA_KERNEL_MERGE = 2
+CSA_KERNEL_KINDS = 3
+KERNEL_NAMES = ("score", "select", "merge")
 
 EXPORTS = ("csa_abi_version", "csa_status_str", "csa_indexer_topk_workspace_size",
            "csa_indexer_topk", "csa_indexer_topk_batched", "csa_profile_enable",
@@ -37,7 +38,7 @@ class CsaError(RuntimeError):
 class csa_opts(ctypes.Structure):
     _fields_ = [("chunk_keys", ctypes.c_int64),
                 ("key_tile", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32),
+                ("key_splits", ctypes.c_int32),
                 ("workspace_budget", ctypes.c_int64),
                 ("reserved", ctypes.c_int64 * 4)]
 
@@ -96,11 +97,12 @@ def abi_version() -> int:
     return load_library().csa_abi_version()
 
 
-def _opts(chunk_keys=0, key_tile=0, workspace_budget=0):
+def _opts(chunk_keys=0, key_tile=0, workspace_budget=0, key_splits=0):
     o = csa_opts()
     o.chunk_keys = int(chunk_keys or 0)
     o.key_tile = int(key_tile or 0)
     o.workspace_budget = int(workspace_budget or 0)
+    o.key_splits = int(key_splits or 0)
     return o
 
 
@@ -113,9 +115,9 @@ def _dtype_code(t: torch.dtype) -> int:
 
 
 def workspace_size(S, T, H, D, m, k, *, q_pos0=0, dtype=torch.bfloat16, chunk_keys=0,
-                   key_tile=0, workspace_budget=0) -> int:
+                   key_tile=0, workspace_budget=0, key_splits=0) -> int:
     out = ctypes.c_size_t(0)
-    o = _opts(chunk_keys, key_tile, workspace_budget)
+    o = _opts(chunk_keys, key_tile, workspace_budget, key_splits)
     _check(load_library().csa_indexer_topk_workspace_size(
         int(S), int(T), int(H), int(D), int(m), int(k), int(q_pos0), _dtype_code(dtype),
         ctypes.byref(o), ctypes.byref(out)))
@@ -124,7 +126,7 @@ def workspace_size(S, T, H, D, m, k, *, q_pos0=0, dtype=torch.bfloat16, chunk_ke
 
 def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
          q_pos0: int = 0, chunk_keys: int = 0, key_tile: int = 0, workspace_budget: int = 0,
-         workspace: torch.Tensor | None = None, out: tuple | None = None):
+         key_splits: int = 0, workspace: torch.Tensor | None = None, out: tuple | None = None):
     """CSA lightning-indexer top-k on the GPU.
 
     q [S, H, D], w [S, H], kc [T, D]: contiguous device tensors, all bfloat16
@@ -165,7 +167,7 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
             raise ValueError("%s must be contiguous" % name)
     dt = _dtype_code(q.dtype)
     lib = load_library()
-    o = _opts(chunk_keys, key_tile, workspace_budget)
+    o = _opts(chunk_keys, key_tile, workspace_budget, key_splits)
     if out is None:
         idx = torch.empty(oshape, dtype=torch.int32, device=dev)
         score = torch.empty(oshape, dtype=torch.float32, device=dev)
@@ -179,7 +181,7 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
     if workspace is None:
         nbytes = workspace_size(S, T, H, D, m, k, q_pos0=q_pos0, dtype=q.dtype,
                                 chunk_keys=chunk_keys, key_tile=key_tile,
-                                workspace_budget=workspace_budget)
+                                workspace_budget=workspace_budget, key_splits=key_splits)
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     else:
         nbytes = workspace.numel() * workspace.element_size()

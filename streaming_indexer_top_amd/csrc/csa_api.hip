@@ -27,6 +27,12 @@ constexpr int64_t kDefaultChunkCap = 65536;  // single chunk up to this many key
 constexpr int64_t kDefaultChunk = 65536;
 constexpr int32_t kDefaultTile = 128;
 constexpr size_t kAlign = 256;
+// Key splits (automatic): used when a problem has fewer query blocks than
+// this (a 256-CU part then has idle CUs), doubled until blocks x splits
+// reaches twice it, capped by kMaxSplits and by kSplitMinKeys keys per split.
+constexpr int64_t kSplitBlocks = 256;
+constexpr int64_t kSplitMinKeys = 2048;
+constexpr int32_t kMaxSplits = 64;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -34,13 +40,15 @@ struct Plan {
     int64_t n_max = 0;   // keys usable by the last row
     int64_t chunk = 0;   // keys per chunk (0: no row has a key)
     int64_t n_chunks = 0;
+    int64_t splits = 1;  // key splits of the (single) chunk, scored and selected in parallel
+    int64_t slen = 0;    // keys per split (== chunk without splits)
     int32_t tile = kDefaultTile;
-    bool lists = false;  // more than one chunk: running lists live in the workspace
+    bool lists = false;  // several chunks or splits: lists live in the workspace
 };
 
 // Workspace layout of a pass of `rows` rows, in this order:
-//   scores [rows][chunk] fp32 | meta [rows] ChunkMeta |
-//   (more than one chunk:) lists [rows][k] u64 | state [rows] RowState
+//   scores [rows][chunk] fp32 | meta [splits*rows] ChunkMeta |
+//   (several chunks or splits:) lists [splits*rows][k] u64 | state [splits*rows] RowState
 struct PassLayout {
     size_t meta, lists, state, end;
 };
@@ -49,12 +57,13 @@ PassLayout pass_layout(const Plan &p, int64_t rows, int64_t k)
 {
     PassLayout l{0, 0, 0, 0};
     if (p.chunk == 0 || rows <= 0) return l;
+    const size_t vrows = (size_t)rows * (size_t)p.splits;
     l.meta = align_up((size_t)rows * (size_t)p.chunk * sizeof(float));
-    l.end = l.meta + align_up((size_t)rows * sizeof(csa::ChunkMeta));
+    l.end = l.meta + align_up(vrows * sizeof(csa::ChunkMeta));
     if (p.lists) {
         l.lists = l.end;
-        l.state = l.lists + align_up((size_t)rows * (size_t)k * sizeof(uint64_t));
-        l.end = l.state + align_up((size_t)rows * sizeof(csa::RowState));
+        l.state = l.lists + align_up(vrows * (size_t)k * sizeof(uint64_t));
+        l.end = l.state + align_up(vrows * sizeof(csa::RowState));
     }
     return l;
 }
@@ -76,24 +85,63 @@ int check_args(int64_t S, int64_t T, int32_t H, int32_t D, int32_t m, int64_t k,
         if (opts->key_tile != 0 && opts->key_tile != 64 && opts->key_tile != 128 &&
             opts->key_tile != 256)
             return CSA_ERR_BAD_OPTION;
-        if (opts->workspace_budget < 0 || opts->reserved0 != 0) return CSA_ERR_BAD_OPTION;
+        if (opts->workspace_budget < 0) return CSA_ERR_BAD_OPTION;
+        const int32_t ks = opts->key_splits;
+        if (ks < 0 || ks > kMaxSplits || (ks & (ks - 1)) != 0) return CSA_ERR_BAD_OPTION;
         for (int i = 0; i < 4; ++i)
             if (opts->reserved[i] != 0) return CSA_ERR_BAD_OPTION;
     }
     return CSA_OK;
 }
 
-Plan make_plan(int64_t S, int64_t T, int32_t m, int64_t q_pos0, const csa_opts *opts)
+int64_t budget_of(const csa_opts *opts)
+{
+    return (opts && opts->workspace_budget) ? opts->workspace_budget : kDefaultBudget;
+}
+
+// The plan: chunks of the usable keys, or, for problems with few query
+// blocks (e.g. decoding a few new queries against a long key cache), one
+// chunk cut into key splits that run in parallel.  Pure host arithmetic.
+Plan make_plan(int64_t S, int64_t T, int32_t m, int64_t q_pos0, int64_t k, int32_t dtype,
+               const csa_opts *opts)
 {
     Plan p;
     p.n_max = S > 0 ? csa::n_usable(q_pos0 + S - 1, T, m) : 0;
     if (opts && opts->key_tile) p.tile = opts->key_tile;
     if (p.n_max == 0) return p;
     const int64_t n_round = (p.n_max + 255) / 256 * 256;
-    int64_t c = (opts && opts->chunk_keys) ? opts->chunk_keys
-                                           : (n_round <= kDefaultChunkCap ? n_round : kDefaultChunk);
+    const bool user_chunk = opts && opts->chunk_keys;
+    const int32_t ks = opts ? opts->key_splits : 0;
+    // Key splits: bf16 only (the fp32 path has no chunk summaries), not with
+    // a chunk size the caller fixed.
+    int64_t g = 1;
+    if (dtype == CSA_BF16 && !user_chunk && ks != 1) {
+        if (ks >= 2) {
+            g = ks;
+        } else {
+            const int64_t nqb = (S + csa::kScoreWaves - 1) / csa::kScoreWaves;
+            if (nqb < kSplitBlocks) {
+                g = 2;
+                while (g < kMaxSplits && nqb * g < 2 * kSplitBlocks) g *= 2;
+                while (g > 1 && p.n_max / g < kSplitMinKeys) g /= 2;
+            }
+        }
+    }
+    if (g > 1) {
+        Plan q = p;
+        q.splits = g;
+        q.slen = ((p.n_max + g - 1) / g + 255) / 256 * 256;
+        q.chunk = g * q.slen;
+        q.n_chunks = 1;
+        q.lists = true;
+        // Automatic splits only where one pass holds every row; else chunks.
+        if (ks >= 2 || pass_bytes(q, S, k) <= (size_t)budget_of(opts)) return q;
+    }
+    int64_t c = user_chunk ? opts->chunk_keys
+                           : (n_round <= kDefaultChunkCap ? n_round : kDefaultChunk);
     if (c > n_round) c = n_round;
     p.chunk = c;
+    p.slen = c;
     p.n_chunks = (p.n_max + c - 1) / c;
     p.lists = p.n_chunks > 1;
     return p;
@@ -103,8 +151,9 @@ Plan make_plan(int64_t S, int64_t T, int32_t m, int64_t q_pos0, const csa_opts *
 int64_t rows_fitting(const Plan &p, int64_t S, int64_t k, size_t bytes)
 {
     if (pass_bytes(p, S, k) <= bytes) return S;
-    const size_t per_row = (size_t)p.chunk * 4 + sizeof(csa::ChunkMeta) +
-                           (p.lists ? (size_t)k * 8 + sizeof(csa::RowState) : 0);
+    const size_t per_row = (size_t)p.chunk * 4 + (size_t)p.splits * sizeof(csa::ChunkMeta) +
+                           (p.lists ? (size_t)p.splits * ((size_t)k * 8 + sizeof(csa::RowState))
+                                    : 0);
     int64_t r = (int64_t)(bytes / per_row);
     r = r / csa::kScoreWaves * csa::kScoreWaves;
     while (r > 0 && pass_bytes(p, r, k) > bytes) r -= csa::kScoreWaves;
@@ -170,7 +219,7 @@ const char *csa_status_str(int status)
     case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small for one query block";
     case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 4096 or T >= 2^31)";
     case CSA_ERR_HIP: return "HIP call or kernel launch failed";
-    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256, key_tile one of 64/128/256, reserved fields 0";
+    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256, key_tile one of 64/128/256, key_splits 0 or a power of two up to 64, reserved fields 0";
     default: return "unknown status";
     }
 }
@@ -182,9 +231,8 @@ int csa_indexer_topk_workspace_size(int64_t S, int64_t T, int32_t H_I, int32_t D
     if (!bytes_out) return CSA_ERR_NULL_PTR;
     int st = check_args(S, T, H_I, D_I, m, k, q_pos0, dtype, opts);
     if (st != CSA_OK) return st;
-    const Plan p = make_plan(S, T, m, q_pos0, opts);
-    const int64_t budget = (opts && opts->workspace_budget) ? opts->workspace_budget : kDefaultBudget;
-    int64_t rows = rows_fitting(p, S, k, (size_t)budget);
+    const Plan p = make_plan(S, T, m, q_pos0, k, dtype, opts);
+    int64_t rows = rows_fitting(p, S, k, (size_t)budget_of(opts));
     const int64_t min_rows = S < csa::kScoreWaves ? S : csa::kScoreWaves;
     if (rows < min_rows) rows = min_rows;
     *bytes_out = pass_bytes(p, rows, k);
@@ -204,7 +252,7 @@ int check_call(const void *q, const void *w, const void *kc, int32_t dtype, int6
 {
     int st = check_args(S, T, H_I, D_I, m, k, q_pos0, dtype, opts);
     if (st != CSA_OK) return st;
-    const Plan p = make_plan(S, T, m, q_pos0, opts);
+    const Plan p = make_plan(S, T, m, q_pos0, k, dtype, opts);
     *plan_out = p;
     *rows_out = 0;
     if (S == 0) return CSA_OK;
@@ -232,7 +280,7 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
     int st = CSA_OK;
     if (S == 0) return CSA_OK;
     if (p.chunk > 0) {
-        if (rows < S) {
+        if (rows < S && p.splits == 1) {
             // Several passes.  Score workgroups of one pass run in rounds of
             // (CUs x workgroups per CU); a partial round leaves CUs idle for
             // a whole workgroup's time, so passes get whole rounds (only the
@@ -256,6 +304,11 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
                 even = (even + csa::kScoreWaves - 1) / csa::kScoreWaves * csa::kScoreWaves;
                 if (even < rows) rows = even;
             }
+        } else if (rows < S) {
+            const int64_t passes = (S + rows - 1) / rows;
+            int64_t even = (S + passes - 1) / passes;
+            even = (even + csa::kScoreWaves - 1) / csa::kScoreWaves * csa::kScoreWaves;
+            if (even < rows) rows = even;
         }
     }
     hipStream_t s = (hipStream_t)stream;
@@ -287,6 +340,7 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
                 sa.T = T;
                 sa.c0 = c0;
                 sa.clen = p.chunk;
+                sa.slen = p.slen;
                 sa.H = H_I;
                 sa.m = m;
                 st = launch_timed(CSA_KERNEL_SCORE, s, [&] {
@@ -307,12 +361,30 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
             se.T = T;
             se.c0 = c0;
             se.clen = p.chunk;
+            se.slen = p.slen;
             se.k = k;
             se.m = m;
+            se.nsplit = (int32_t)p.splits;
             se.first = c == 0;
-            se.emit = c == nch - 1;
+            // With splits every split's best k goes to its own list; the
+            // merge rounds below combine them and write the outputs.
+            se.emit = c == nch - 1 && p.splits == 1;
             st = launch_timed(CSA_KERNEL_SELECT, s, [&] { return csa::launch_select(se, s); });
             if (st != CSA_OK) return st;
+            for (int64_t half = p.splits / 2; half >= 1; half /= 2) {
+                csa::MergeArgs mg;
+                mg.lists = lists;
+                mg.state = state;
+                mg.out_idx = idx;
+                mg.out_score = score;
+                mg.row0 = r0;
+                mg.rows = nr;
+                mg.k = k;
+                mg.half = (int32_t)half;
+                mg.emit = half == 1;
+                st = launch_timed(CSA_KERNEL_MERGE, s, [&] { return csa::launch_merge(mg, s); });
+                if (st != CSA_OK) return st;
+            }
         }
     }
     return CSA_OK;

@@ -61,31 +61,53 @@ struct ScoreArgs {
     int64_t T;
     int64_t c0;       // first key of the chunk
     int64_t clen;     // chunk length in keys; also the ws row stride
+    int64_t slen;     // keys per split (grid.y splits the chunk; slen == clen: no split)
     int32_t H;
     int32_t m;
 };
 
 // One pass of the select kernel over the same batch and chunk.
+//
+// With splits (nsplit > 1) every (split y, row r) pair is a virtual row
+// y*rows + r that selects among the split's keys [c0 + y*slen, +slen) and
+// leaves its sorted best k in lists / state at that index (first = 1,
+// emit = 0); the merge kernel then combines the splits' lists.
 struct SelectArgs {
     const float *ws;      // [rows][clen] scores written by the score pass
-    const ChunkMeta *meta;  // [rows] chunk summaries, or null (then no shortcut)
-    uint64_t *lists;      // [rows][k] running best-k lists, sorted descending
-    RowState *state;      // [rows] running list length and k-th key
+    const ChunkMeta *meta;  // [nsplit*rows] chunk summaries, or null (then no shortcut)
+    uint64_t *lists;      // [nsplit*rows][k] running best-k lists, sorted descending
+    RowState *state;      // [nsplit*rows] running list length and k-th key
     int32_t *out_idx;     // [S][k]
     float *out_score;     // [S][k]
     int64_t row0, rows, q_pos0, T;
     int64_t c0, clen;
+    int64_t slen;         // keys per split (== clen without splits)
     int64_t k;
     int32_t m;
+    int32_t nsplit;       // splits of the chunk (1: none)
     int32_t first;        // 1: no earlier chunk, the running lists start empty
     int32_t emit;         // 1: last chunk, sort the lists and write the outputs
+};
+
+// One round of the merge of split lists: for p < half, the lists of virtual
+// rows p*rows + r and (p+half)*rows + r are merged into the first; with
+// emit (half == 1) the merged best k are written as the row's outputs.
+struct MergeArgs {
+    uint64_t *lists;      // [splits*rows][k]
+    RowState *state;      // [splits*rows]
+    int32_t *out_idx;     // [S][k]
+    float *out_score;     // [S][k]
+    int64_t row0, rows, k;
+    int32_t half;
+    int32_t emit;
 };
 
 // Dtype codes as in the public header.
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
-// Score kernel: grid ceil(rows/8) workgroups for bf16 (each covers the whole
-// chunk for its 8 rows) or (rows x ceil(clen/256)) for fp32.
+// Score kernel: grid ceil(rows/8) x splits workgroups for bf16 (each covers
+// its split of the chunk for its 8 rows; the chunk summary of row r in split
+// y goes to meta[y*rows + r]) or (rows x ceil(clen/256)) for fp32 (no splits).
 hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t key_tile,
                         hipStream_t stream);
 
@@ -93,8 +115,11 @@ hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t ke
 // error), for sizing passes in whole rounds of workgroups.
 int score_blocks_per_cu(int32_t dtype, int32_t D, int32_t H, int32_t key_tile);
 
-// Select kernel: one workgroup per row of the batch.
+// Select kernel: one workgroup per (virtual) row of the batch.
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
+
+// Merge kernel: one workgroup per (row, list pair) of a merge round.
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
 // Keys of one chunk piece that the select kernel stages in LDS at a time.
 constexpr int kSelectPiece = 2048;

@@ -130,8 +130,10 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     const bool active = rl < a.rows;
     const int64_t last = min(qb * WAVES + WAVES - 1, a.rows - 1);
     const int64_t n_hi = n_usable(a.q_pos0 + a.row0 + last, a.T, a.m);
-    const int64_t kb0 = a.c0;
-    const int64_t kcap = a.c0 + a.clen;
+    // Keys of this workgroup: split blockIdx.y of the chunk.
+    const int64_t split = (int64_t)blockIdx.y;
+    const int64_t kb0 = a.c0 + split * a.slen;
+    const int64_t kcap = min(a.c0 + a.clen, kb0 + a.slen);
     const int64_t k_end = min(kcap, n_hi);
     if (kb0 >= k_end) return;  // uniform: no row of this block has a key here
     const int64_t my_end =
@@ -274,8 +276,8 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
 
     // Scores are stored and counted 64 keys at a time (2 blocks): chunk-
     // relative 32-bit key offsets, one lane per key.
-    float *wsrow = a.ws + (active ? rl : 0) * a.clen;
-    const __amdgpu_buffer_rsrc_t ws_rs = buffer_rsrc(wsrow, (uint32_t)(a.clen * 4));
+    float *wsrow = a.ws + (active ? rl : 0) * a.clen + split * a.slen;
+    const __amdgpu_buffer_rsrc_t ws_rs = buffer_rsrc(wsrow, (uint32_t)((kcap - kb0) * 4));
     const int my_len = (int)(my_end - kb0);  // keys of this row in the chunk
     const float f_floor = filt ? key_score_of(u_floor) : 0.0f;
     uint32_t *h = hist_all + wave * kHistBins;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     // key 64p + l, summed as (lanes 0-31 share) + (lanes 32-63 share).
     // Branch-free, so that the tile stays one scheduling region: lanes past
     // the row's last key store into unused slots of the row (tiles never run
-    // past the chunk, whose length is a multiple of NT) and add 0 to the
+    // past the split, whose length is a multiple of NT) and add 0 to the
     // histogram.
     auto finish2 = [&](float pe, float po, int rel0, bool real) {
         const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe), __float_as_uint(po),
@@ -434,10 +436,10 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
                     }
                     above += c;
                 }
-                a.meta[rl] = m;
+                a.meta[split * a.rows + rl] = m;
             }
         } else if (lane == 0) {
-            a.meta[rl] = m;
+            a.meta[split * a.rows + rl] = m;
         }
     }
 }
@@ -493,7 +495,8 @@ hipError_t launch_bf16_cfg(const ScoreArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const dim3 grid((unsigned)((a.rows + WAVES - 1) / WAVES));
+    const dim3 grid((unsigned)((a.rows + WAVES - 1) / WAVES),
+                    (unsigned)((a.clen + a.slen - 1) / a.slen));
     score_bf16_kernel<D, HT, NT, DB, WAVES><<<grid, WAVES * 64, lds, s>>>(a);
     return hipGetLastError();
 }

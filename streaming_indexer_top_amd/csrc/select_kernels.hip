@@ -650,6 +650,92 @@ __device__ __noinline__ int collect_pieces(uint64_t *cand, const RowCtx r, int k
     return cnt;
 }
 
+// This thread's share of the merge of two descending lists L[0..nl) and
+// Q[0..nq): the entries at positions p0..p0+PT-1 of the merged order, up to
+// position `total`, in outv (merge-path split: a binary search for how many
+// entries of L come before p0, then a sequential merge).  Returns how many
+// it produced; kth receives the entry at position kpos if this thread has it.
+template <int PT>
+__device__ inline int merge_share(const uint64_t *L, int nl, const uint64_t *Q, int nq, int total,
+                                  int p0, int kpos, uint64_t (&outv)[PT], uint64_t &kth)
+{
+    int nout = 0;
+#pragma unroll
+    for (int t = 0; t < PT; ++t) outv[t] = 0ull;
+    if (p0 < total) {
+        int lo = max(0, p0 - nq), hi = min(p0, nl);
+        while (lo < hi) {  // i = entries taken from L before position p0
+            const int mid = (lo + hi) >> 1;
+            if (L[mid] > Q[p0 - 1 - mid]) lo = mid + 1;
+            else hi = mid;
+        }
+        int i = lo, j = p0 - lo;
+#pragma unroll
+        for (int t = 0; t < PT; ++t) {
+            if (p0 + t < total) {
+                uint64_t v;
+                if (j >= nq || (i < nl && L[i] > Q[j])) v = L[i++];
+                else v = Q[j++];
+                outv[t] = v;
+                if (p0 + t == kpos) kth = v;
+                ++nout;
+            }
+        }
+    }
+    return nout;
+}
+
+// Writes positions p0..p0+PT-1 (below k) of a row's outputs: the first nout
+// from outv, then padding (idx -1, score -inf).  16-byte stores when aligned.
+template <int PT>
+__device__ inline void emit_share(int32_t *oi, float *os, int k, int p0, const uint64_t (&outv)[PT],
+                                  int nout)
+{
+    int32_t vi[PT];
+    float vs[PT];
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+        vi[t] = t < nout ? key_index(outv[t]) : -1;
+        vs[t] = t < nout ? key_score(outv[t]) : -__builtin_inff();
+    }
+    const bool al16 = ((((uintptr_t)oi) | ((uintptr_t)os)) & 15u) == 0u;
+    if (al16 && p0 + PT <= k) {  // 16-byte aligned, whole
+#pragma unroll
+        for (int t = 0; t < PT; t += 4) {
+            *(int4 *)(oi + p0 + t) = make_int4(vi[t], vi[t + 1], vi[t + 2], vi[t + 3]);
+            *(float4 *)(os + p0 + t) = make_float4(vs[t], vs[t + 1], vs[t + 2], vs[t + 3]);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < PT; ++t) {
+            if (p0 + t < k) {
+                oi[p0 + t] = vi[t];
+                os[p0 + t] = vs[t];
+            }
+        }
+    }
+}
+
+// Writes this thread's share (positions p0.., nout entries) of a list of k
+// slots; `whole`: all PT entries are real.
+template <int PT>
+__device__ inline void store_share(uint64_t *dst, int k, int p0, const uint64_t (&outv)[PT], int nout)
+{
+    if ((k & 1) == 0 && nout == PT) {  // 16-byte aligned, whole
+#pragma unroll
+        for (int t = 0; t < PT; t += 2) {
+            ulonglong2 v2;
+            v2.x = outv[t];
+            v2.y = outv[t + 1];
+            *(ulonglong2 *)(dst + p0 + t) = v2;
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < PT; ++t)
+            if (t < nout) dst[p0 + t] = outv[t];
+    }
+}
+
 template <int K>
 __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArgs a)
 {
@@ -661,11 +747,16 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
     uint64_t *cand = smem;                                 // Caps<K>::Cand keys
     uint32_t *bk = (uint32_t *)(smem + Caps<K>::Cand);    // bucket words (also a 256-bin histogram)
     const int tid = threadIdx.x;
-    const int64_t rl = a.rows - 1 - (int64_t)blockIdx.x;  // long rows first
+    // Virtual row vr = split * rows + rl (split 0 and vr == rl without
+    // splits); long rows first.
+    const int64_t split = (int64_t)blockIdx.x / a.rows;
+    const int64_t rl = a.rows - 1 - ((int64_t)blockIdx.x - split * a.rows);
+    const int64_t vr = split * a.rows + rl;
     const int64_t row = a.row0 + rl;
     const int64_t n = n_usable(a.q_pos0 + row, a.T, a.m);
-    int64_t len = n - a.c0;
-    len = len < 0 ? 0 : (len > a.clen ? a.clen : len);
+    const int64_t c0 = a.c0 + split * a.slen;  // first key of the split
+    int64_t len = n - c0;
+    len = len < 0 ? 0 : (len > a.slen ? a.slen : len);
     // Nothing to add and nothing to write: the running list stays as it is.
     // (The first chunk always runs so that every row's state is written.)
     if (!a.emit && !a.first && len == 0) return;
@@ -673,15 +764,15 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
     int cnt_l = 0;
     uint64_t theta = 0;
     if (!a.first) {
-        const RowState stt = a.state[rl];
+        const RowState stt = a.state[vr];
         cnt_l = stt.count;
         theta = stt.theta;
     }
 
     RowCtx r;
-    r.src = a.ws + rl * a.clen;
+    r.src = a.ws + rl * a.clen + split * a.slen;
     r.len = len;
-    r.c0 = (uint32_t)a.c0;
+    r.c0 = (uint32_t)c0;
     r.filt = theta != 0;
     r.f_floor = score_of_orderable((uint32_t)(theta >> 32));
 
@@ -692,7 +783,7 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
         int nA = 0, nB = 0;
         bool done = false;
         if (a.meta) {
-            const ChunkMeta mt = a.meta[rl];
+            const ChunkMeta mt = a.meta[vr];
             if (mt.total <= (uint32_t)k) {
                 // Every key that beats the floor (at most k of them).
                 collect<K>(r, -__builtin_inff(), __builtin_inff(), cand, sh, tid, nA, nB);
@@ -732,98 +823,83 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
     // Running list into the B region (free once the sort is done).
     uint64_t *lst = cand + kCapA;
     if (cnt_l > 0) {
-        const uint64_t *src = a.lists + rl * a.k;
+        const uint64_t *src = a.lists + vr * a.k;
         for (int e = tid; e < cnt_l; e += NT) lst[e] = src[e];
     }
     __syncthreads();
 
     // Merge with the running list (both sorted descending) and keep the
-    // first min(k, |L| + |Q|) entries: merge-path split, 8 outputs per thread.
+    // first min(k, |L| + |Q|) entries: merge-path split, PT outputs per thread.
     const int total = min(k, cnt_l + cnt_q);
     constexpr int PT = Caps<K>::PT;  // outputs per thread (k <= K)
     const int p0 = tid * PT;
     uint64_t outv[PT];
     uint64_t kth = 0;  // the entry at position k-1, for the next chunk's floor
-    int nout = 0;
-#pragma unroll
-    for (int t = 0; t < PT; ++t) outv[t] = 0ull;
-    if (p0 < total) {
-        int lo = max(0, p0 - cnt_q), hi = min(p0, cnt_l);
-        while (lo < hi) {  // i = entries taken from L before position p0
-            const int mid = (lo + hi) >> 1;
-            if (lst[mid] > cand[p0 - 1 - mid]) lo = mid + 1;
-            else hi = mid;
-        }
-        int i = lo, j = p0 - lo;
-#pragma unroll
-        for (int t = 0; t < PT; ++t) {
-            if (p0 + t < total) {
-                uint64_t v;
-                if (j >= cnt_q || (i < cnt_l && lst[i] > cand[j])) v = lst[i++];
-                else v = cand[j++];
-                outv[t] = v;
-                if (p0 + t == k - 1) kth = v;
-                ++nout;
-            }
+    const int nout = merge_share<PT>(lst, cnt_l, cand, cnt_q, total, p0, k - 1, outv, kth);
+    if (a.emit) {
+        // NT*PT = K >= k, so every position is written.
+        emit_share<PT>(a.out_idx + row * a.k, a.out_score + row * a.k, k, p0, outv, nout);
+    } else {
+        store_share<PT>(a.lists + vr * a.k, k, p0, outv, nout);
+        if (total == k && p0 <= k - 1 && k - 1 < p0 + nout) a.state[vr].theta = kth;
+        if (tid == 0) {
+            a.state[vr].count = total;
+            if (total < k) a.state[vr].theta = 0;
         }
     }
+}
+
+// One merge round of split lists (see MergeArgs): workgroup (p, rl) merges
+// the lists of virtual rows p*rows + rl and (p+half)*rows + rl.
+template <int K>
+__global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a)
+{
+    extern __shared__ uint64_t smem[];
+    const int tid = threadIdx.x;
+    const int k = (int)a.k;
+    const int64_t p = (int64_t)blockIdx.x / a.rows;
+    const int64_t rl = a.rows - 1 - ((int64_t)blockIdx.x - p * a.rows);
+    const int64_t va = p * a.rows + rl, vb = (p + a.half) * a.rows + rl;
+    const int na = a.state[va].count, nb = a.state[vb].count;
+    uint64_t *la = smem, *lb = smem + K;
+    for (int e = tid; e < na; e += NT) la[e] = a.lists[va * a.k + e];
+    for (int e = tid; e < nb; e += NT) lb[e] = a.lists[vb * a.k + e];
+    __syncthreads();
+    const int total = min(k, na + nb);
+    constexpr int PT = Caps<K>::PT;
+    const int p0 = tid * PT;
+    uint64_t outv[PT];
+    uint64_t kth = 0;
+    const int nout = merge_share<PT>(la, na, lb, nb, total, p0, k - 1, outv, kth);
     if (a.emit) {
-        int32_t *oi = a.out_idx + row * a.k;
-        float *os = a.out_score + row * a.k;
-        int32_t vi[PT];
-        float vs[PT];
-#pragma unroll
-        for (int t = 0; t < PT; ++t) {
-            vi[t] = t < nout ? key_index(outv[t]) : -1;
-            vs[t] = t < nout ? key_score(outv[t]) : -__builtin_inff();
-        }
-        const bool al16 = ((((uintptr_t)oi) | ((uintptr_t)os)) & 15u) == 0u;
-        if (al16 && p0 + PT <= k) {  // 16-byte aligned, whole
-#pragma unroll
-            for (int t = 0; t < PT; t += 4) {
-                *(int4 *)(oi + p0 + t) = make_int4(vi[t], vi[t + 1], vi[t + 2], vi[t + 3]);
-                *(float4 *)(os + p0 + t) = make_float4(vs[t], vs[t + 1], vs[t + 2], vs[t + 3]);
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < PT; ++t) {
-                if (p0 + t < k) {
-                    oi[p0 + t] = vi[t];
-                    os[p0 + t] = vs[t];
-                }
-            }
-        }
-        // NT*PT = K >= k, so every position is written.
+        const int64_t row = a.row0 + rl;
+        emit_share<PT>(a.out_idx + row * a.k, a.out_score + row * a.k, k, p0, outv, nout);
     } else {
-        uint64_t *dst = a.lists + rl * a.k;
-        if ((k & 1) == 0 && p0 + PT <= total) {  // 16-byte aligned, whole
-#pragma unroll
-            for (int t = 0; t < PT; t += 2) {
-                ulonglong2 v2;
-                v2.x = outv[t];
-                v2.y = outv[t + 1];
-                *(ulonglong2 *)(dst + p0 + t) = v2;
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < PT; ++t)
-                if (t < nout) dst[p0 + t] = outv[t];
-        }
-        if (total == k && p0 <= k - 1 && k - 1 < p0 + nout) a.state[rl].theta = kth;
-        if (tid == 0) {
-            a.state[rl].count = total;
-            if (total < k) a.state[rl].theta = 0;
-        }
+        store_share<PT>(a.lists + va * a.k, k, p0, outv, nout);
+        if (tid == 0) a.state[va].count = total;
     }
 }
 
 }  // namespace
 
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream)
+{
+    if (a.rows <= 0 || a.half <= 0) return hipSuccess;
+    const dim3 grid((unsigned)(a.rows * a.half));
+    if (a.k <= 2048) {
+        merge_kernel<2048><<<grid, dim3(NT), 2 * 2048 * sizeof(uint64_t), stream>>>(a);
+    } else {
+        merge_kernel<4096><<<grid, dim3(NT), 2 * 4096 * sizeof(uint64_t), stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0) return hipSuccess;
+    const dim3 grid((unsigned)(a.rows * a.nsplit));
     if (a.k <= 2048) {
-        select_kernel<2048><<<dim3((unsigned)a.rows), dim3(NT), Caps<2048>::lds_bytes, stream>>>(a);
+        select_kernel<2048><<<grid, dim3(NT), Caps<2048>::lds_bytes, stream>>>(a);
     } else {
         static bool attr_set = false;  // benign race: every caller sets the same value
         if (!attr_set) {
@@ -833,7 +909,7 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
             if (e != hipSuccess) return e;
             attr_set = true;
         }
-        select_kernel<4096><<<dim3((unsigned)a.rows), dim3(NT), Caps<4096>::lds_bytes, stream>>>(a);
+        select_kernel<4096><<<grid, dim3(NT), Caps<4096>::lds_bytes, stream>>>(a);
     }
     return hipGetLastError();
 }

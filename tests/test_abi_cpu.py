@@ -8,6 +8,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import streaming_indexer_top_amd as csa
 from streaming_indexer_top_amd import binding
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = csa.load_library()
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
     for st in range(0, 10):
         assert lib.csa_status_str(st)
 
@@ -61,6 +62,23 @@ def test_workspace_zero_without_usable_keys():
 def test_workspace_single_chunk_when_small():
     # 1024 rows, last row sees 256 keys: one chunk of 256 keys, no lists.
     assert _ws(1024, 256, H=4, D=32, k=16) == 1024 * 256 * 4 + 1024 * 16
+
+
+def test_key_splits_for_few_rows():
+    # 64 decode rows against 262144 keys: one chunk of all keys cut into
+    # splits, each with its own list -> scores + 64 splits x 64 rows x (16 B
+    # summary + k*8 B list + 16 B state), within the default budget.
+    b = _ws(64, 1 << 18, q_pos0=(1 << 20) - 64)
+    per_split_row = 16 + 2048 * 8 + 16
+    assert b >= 64 * (1 << 18) * 4 + 64 * 64 * per_split_row
+    # Splits off: one 65536-key chunk at a time with one running list per row.
+    b1 = _ws(64, 1 << 18, q_pos0=(1 << 20) - 64, key_splits=1)
+    assert b1 == 64 * 65536 * 4 + 1024 + 64 * 2048 * 8 + 1024
+    # Many rows: no splits (same as key_splits=1).
+    assert _ws(1 << 14, 1 << 12) == _ws(1 << 14, 1 << 12, key_splits=1)
+    # fp32: never split.
+    assert _ws(64, 1 << 18, q_pos0=(1 << 20) - 64, dtype=torch.float32) == \
+        _ws(64, 1 << 18, q_pos0=(1 << 20) - 64, dtype=torch.float32, key_splits=1)
 
 
 def test_workspace_tiny_budget_still_fits_one_block():
@@ -130,7 +148,7 @@ def test_workspace_too_small():
 def test_bad_options():
     lib = csa.load_library()
     for field, val in (("chunk_keys", 100), ("key_tile", 96), ("workspace_budget", -1),
-                       ("reserved0", 1)):
+                       ("key_splits", 3), ("key_splits", 128), ("key_splits", -2)):
         o = binding.csa_opts()
         setattr(o, field, val)
         assert _call(lib, opts=o) == 8, field

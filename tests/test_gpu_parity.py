@@ -255,6 +255,43 @@ def test_batched_bf16_matches_single_calls_multi_pass():
             assert np.array_equal(s_sc.view(np.uint32), g_sc[b].view(np.uint32))
 
 
+@pytest.mark.parametrize("k", [512, 4096])
+def test_key_splits_integer_bit_exact(k):
+    """Few rows against many keys (decode shape): the keys are split, each
+    split selects its own best k, the lists are merged pairwise.  Automatic
+    and forced split counts, and several passes, all equal the oracle."""
+    S, T, H, D, m = 64, 20000, 64, 128, 1
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=50, dtype=torch.bfloat16, signed_w=True)
+    q_pos0 = T - 40  # rows see 19961..20000 keys (the last 24 rows all of them)
+    say("key splits integer S=%d T=%d k=%d" % (S, T, k))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    for splits, budget in ((0, 0), (1, 0), (2, 0), (16, 0), (64, 0), (4, 1)):
+        say("  key_splits=%d budget=%d" % (splits, budget))
+        g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, key_splits=splits,
+                               workspace_budget=budget)
+        assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
+def test_key_splits_bf16_decode():
+    """32 new queries at the end of a 2^20-token sequence (262144 compressed
+    keys): split plan against the oracle, and bit-identical to the unsplit
+    (chunked) plan."""
+    S, T, H, D, m, k = 32, 262144, 64, 128, 4, 2048
+    q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=51)
+    q_pos0 = 4 * T - S
+    say("decode bf16 S=%d T=%d k=%d" % (S, T, k))
+    a_idx, a_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    b_idx, b_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, key_splits=1)
+    assert np.array_equal(a_idx, b_idx)
+    assert np.array_equal(a_sc.view(np.uint32), b_sc.view(np.uint32))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    fails, stats = checks.check_float(a_idx, a_sc, o_idx, o_sc, q.float().numpy(),
+                                      w.float().numpy(), kc.float().numpy(),
+                                      np.arange(S) + q_pos0, T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
 def test_small_workspace_many_passes():
     S, T, H, D, m, k = 2000, 500, 8, 64, 4, 64
     q, w, kc = inputs.integer_valued(S, T, H, D, seed=6, dtype=torch.bfloat16, signed_w=True)

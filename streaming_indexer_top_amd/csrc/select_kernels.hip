@@ -816,7 +816,14 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
             nA = collect_pieces<K>(cand, r, k, bk, sh, tid);
             nB = 0;
         }
-        if (nA + nB > 1) sort_keys<K>(cand, nA, nB, bk, sh, tid);
+        if (nA + nB > 1) {
+            sort_keys<K>(cand, nA, nB, bk, sh, tid);
+        } else if (nB == 1) {
+            // A single key (k = 1), found in region B: the sort would have
+            // moved it to the front.
+            if (tid == 0) cand[0] = cand[kCapA];
+            __syncthreads();
+        }
         cnt_q = min(k, nA + nB);
     }
 

@@ -292,6 +292,47 @@ def test_key_splits_bf16_decode():
     assert_no_fail(fails)
 
 
+@pytest.mark.parametrize("chunk", [0, 256])
+def test_k1_bit_exact(chunk):
+    """k = 1: the single best key often lies in the boundary bin alone."""
+    S, T, H, D, m, k = 1121, 2447, 17, 128, 8, 1
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=60, dtype=torch.bfloat16, signed_w=True)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=1168, chunk_keys=chunk)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=1168)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
+def _random_config(rng):
+    dt = torch.bfloat16 if rng.random() < 0.75 else torch.float32
+    D = int(rng.choice([32, 64, 128]))
+    H = int(rng.choice([1, 3, 17, 32, 33, 64]))
+    m = int(rng.integers(1, 9))
+    S = int(rng.integers(1, 1500))
+    T = int(rng.integers(0, 4000))
+    q_pos0 = int(rng.integers(0, 3000)) if rng.random() < 0.5 else 0
+    k = int(rng.choice([1, 7, 64, 300, 2048, 2049, 4096]))
+    opts = dict(chunk_keys=int(rng.choice([0, 0, 256, 1024])),
+                key_tile=int(rng.choice([0, 64, 128, 256])),
+                key_splits=int(rng.choice([0, 0, 1, 2, 8])),
+                workspace_budget=int(rng.choice([0, 0, 1, 1 << 20])))
+    return dt, S, T, H, D, m, k, q_pos0, opts
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_configs_integer_bit_exact(case):
+    """Seeded random shapes, causal offsets, k, dtypes and options (chunks,
+    tiles, key splits, tiny workspaces): integer inputs equal the oracle bit
+    for bit."""
+    rng = np.random.default_rng(1000 + case)
+    dt, S, T, H, D, m, k, q_pos0, opts = _random_config(rng)
+    say("random case %d: %s S=%d T=%d H=%d D=%d m=%d k=%d q_pos0=%d %s"
+        % (case, dt, S, T, H, D, m, k, q_pos0, opts))
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=2000 + case, dtype=dt, signed_w=True)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, **opts)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
 def test_small_workspace_many_passes():
     S, T, H, D, m, k = 2000, 500, 8, 64, 4, 64
     q, w, kc = inputs.integer_valued(S, T, H, D, seed=6, dtype=torch.bfloat16, signed_w=True)

@@ -333,6 +333,33 @@ def test_random_configs_integer_bit_exact(case):
     assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
 
 
+@pytest.mark.parametrize("case", range(20))
+def test_random_configs_bf16_gaussian(case):
+    """Seeded random V4-shaped bf16 problems with long rows (up to 30000
+    keys: boundary refinement, running lists, key splits), checked by the
+    tolerance rules on up to 64 sampled rows."""
+    rng = np.random.default_rng(3000 + case)
+    S = int(rng.integers(1, 4000))
+    T = int(rng.integers(1, 30000))
+    m = int(rng.choice([1, 2, 4, 8]))
+    q_pos0 = int(rng.integers(0, 20000)) if rng.random() < 0.5 else 0
+    k = int(rng.choice([1, 16, 500, 2048, 3000, 4096]))
+    opts = dict(chunk_keys=int(rng.choice([0, 0, 4096, 16384])),
+                key_tile=int(rng.choice([0, 64, 128, 256])),
+                key_splits=int(rng.choice([0, 0, 1, 4, 16])),
+                workspace_budget=int(rng.choice([0, 0, 1 << 24])))
+    say("gaussian case %d: S=%d T=%d m=%d k=%d q_pos0=%d %s" % (case, S, T, m, k, q_pos0, opts))
+    q, w, kc = inputs.bf16_gaussian(S, T, 64, 128, seed=4000 + case)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, **opts)
+    rows = np.unique(np.concatenate([[0, S - 1], rng.integers(0, S, 62)]))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, rows=rows, q_pos0=q_pos0)
+    fails, stats = checks.check_float(g_idx[rows], g_sc[rows], o_idx, o_sc,
+                                      q.float().numpy()[rows], w.float().numpy()[rows],
+                                      kc.float().numpy(), rows + q_pos0, T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
 def test_small_workspace_many_passes():
     S, T, H, D, m, k = 2000, 500, 8, 64, 4, 64
     q, w, kc = inputs.integer_valued(S, T, H, D, seed=6, dtype=torch.bfloat16, signed_w=True)

@@ -465,20 +465,21 @@ struct RowCtx {
     float f_floor;
 };
 
-// Loads 16 consecutive scores of a workspace row at `base` if base < len.
-// Stays inside the row: base is a multiple of 16 below len <= clen, and clen
-// is a multiple of 256.
+// Loads 16 consecutive scores of a workspace row at `base`; at or past len
+// it loads the row's first 16 instead (callers ignore positions >= len).
+// Unconditional, so that the compiler can count the loads in flight and wait
+// only for the ones it needs.  Stays inside the row: base is a multiple of
+// 16 below len <= row length, which is a multiple of 256.
 __device__ inline void load16(const float *src, int64_t len, int64_t base, float (&v)[16])
 {
-    if (base < len) {
+    const float *p = src + (base < len ? base : 0);
 #pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-            const float4 x = *(const float4 *)(src + base + i);
-            v[i] = x.x;
-            v[i + 1] = x.y;
-            v[i + 2] = x.z;
-            v[i + 3] = x.w;
-        }
+    for (int i = 0; i < 16; i += 4) {
+        const float4 x = *(const float4 *)(p + i);
+        v[i] = x.x;
+        v[i + 1] = x.y;
+        v[i + 2] = x.z;
+        v[i + 3] = x.w;
     }
 }
 
@@ -540,19 +541,23 @@ __device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_e
             }
         }
     };
-    float cur[V], nx1[V], nx2[V];
+    // Three buffers rotate by name (the loop is unrolled by three): a copy
+    // between buffers would wait for the load just issued into the source.
+    float b0[V], b1[V], b2[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) cur[i] = nx1[i] = nx2[i] = 0.0f;
-    load16(r.src, r.len, (int64_t)tid * V, cur);
-    load16(r.src, r.len, ROUND + (int64_t)tid * V, nx1);
-    for (int64_t e0 = 0; e0 < r.len; e0 += ROUND) {
-        load16(r.src, r.len, e0 + 2 * ROUND + (int64_t)tid * V, nx2);
-        process(cur, e0 + (int64_t)tid * V);
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            cur[i] = nx1[i];
-            nx1[i] = nx2[i];
-        }
+    for (int i = 0; i < V; ++i) b0[i] = b1[i] = b2[i] = 0.0f;
+    const int64_t lane0 = (int64_t)tid * V;
+    load16(r.src, r.len, lane0, b0);
+    load16(r.src, r.len, ROUND + lane0, b1);
+    for (int64_t e0 = 0; e0 < r.len; e0 += 3 * ROUND) {
+        load16(r.src, r.len, e0 + 2 * ROUND + lane0, b2);
+        process(b0, e0 + lane0);
+        if (e0 + ROUND >= r.len) break;  // uniform
+        load16(r.src, r.len, e0 + 3 * ROUND + lane0, b0);
+        process(b1, e0 + ROUND + lane0);
+        if (e0 + 2 * ROUND >= r.len) break;
+        load16(r.src, r.len, e0 + 4 * ROUND + lane0, b1);
+        process(b2, e0 + 2 * ROUND + lane0);
     }
     __syncthreads();
     nA = (int)min(sh.nA, (uint32_t)kCapA);
@@ -575,22 +580,27 @@ __device__ __forceinline__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, 
     const bool top = hi_u == 0u;  // the bin reaches the top of the orderable range
     constexpr int V = 16;
     constexpr int ROUND = NT * V;
-    float cur[V], nxt[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) cur[i] = nxt[i] = 0.0f;
-    load16(r.src, r.len, (int64_t)tid * V, cur);
-    for (int64_t e0 = 0; e0 < r.len; e0 += ROUND) {
-        load16(r.src, r.len, e0 + ROUND + (int64_t)tid * V, nxt);
-        const int64_t base = e0 + (int64_t)tid * V;
+    auto count = [&](const float (&v)[V], int64_t base) {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            const float x = cur[i];
+            const float x = v[i];
             const bool in = base + i < r.len && (!r.filt || x > r.f_floor) && x >= f_lo &&
                             (top || !(x >= f_hi));
             hist_add(hist, in, (orderable(x) >> (shift - 8)) & 255u, lane);
         }
+    };
+    // Two buffers rotating by name (unrolled by two), as in collect().
+    float b0[V], b1[V];
 #pragma unroll
-        for (int i = 0; i < V; ++i) cur[i] = nxt[i];
+    for (int i = 0; i < V; ++i) b0[i] = b1[i] = 0.0f;
+    const int64_t lane0 = (int64_t)tid * V;
+    load16(r.src, r.len, lane0, b0);
+    for (int64_t e0 = 0; e0 < r.len; e0 += 2 * ROUND) {
+        load16(r.src, r.len, e0 + ROUND + lane0, b1);
+        count(b0, e0 + lane0);
+        if (e0 + ROUND >= r.len) break;  // uniform
+        load16(r.src, r.len, e0 + 2 * ROUND + lane0, b0);
+        count(b1, e0 + ROUND + lane0);
     }
     __syncthreads();
     find_digit(hist, need, sh, tid);

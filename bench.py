@@ -42,6 +42,8 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_bf16_S65536_hbm_traffic.txt")
 SCORE_SOURCES = ("streaming_indexer_top_amd/csrc/score_kernels.hip",
                  "streaming_indexer_top_amd/csrc/csa_internal.h")
+SELECT_SOURCES = ("streaming_indexer_top_amd/csrc/select_kernels.hip",
+                  "streaming_indexer_top_amd/csrc/csa_internal.h")
 
 
 def pair_count(S, T, m, q_pos0=0):
@@ -49,13 +51,17 @@ def pair_count(S, T, m, q_pos0=0):
     return int(np.minimum(T, (i + 1) // m).sum())
 
 
-def score_source_hash():
-    """sha256 over the sources that define the score kernel."""
+def source_hash(sources=SCORE_SOURCES):
+    """sha256 over the sources that define a kernel."""
     h = hashlib.sha256()
-    for rel in SCORE_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def score_source_hash():
+    return source_hash(SCORE_SOURCES)
 
 
 def read_traffic():
@@ -69,9 +75,14 @@ def read_traffic():
     kv = {a.strip(): b.strip() for a, b in kv.items()}
     if kv.get("source_sha256") != score_source_hash():
         return None
-    return {"bytes": float(kv["traffic_bytes_per_launch"]),
-            "fetch": float(kv["fetch_bytes_per_launch"]),
-            "write": float(kv["write_bytes_per_launch"])}
+    out = {"bytes": float(kv["traffic_bytes_per_launch"]),
+           "fetch": float(kv["fetch_bytes_per_launch"]),
+           "write": float(kv["write_bytes_per_launch"]), "select": None}
+    if kv.get("select_source_sha256") == source_hash(SELECT_SOURCES) and \
+            "select_fetch_bytes_per_launch" in kv:
+        out["select"] = (float(kv["select_fetch_bytes_per_launch"]),
+                         float(kv["select_write_bytes_per_launch"]))
+    return out
 
 
 def summarize_counters(fetch_csv, write_csv, copy_bytes):
@@ -113,10 +124,39 @@ def summarize_counters(fetch_csv, write_csv, copy_bytes):
     if f_se and len(f_se) == len(w_se):
         m = len(f_se)
         out += [
+            "select_source_sha256: %s" % source_hash(SELECT_SOURCES),
             "select_launches: %d" % m,
             "select_fetch_bytes_per_launch: %.0f" % (sum(f_se) * ff * 1024.0 / m),
             "select_write_bytes_per_launch: %.0f" % (sum(w_se) * wf * 1024.0 / m),
         ]
+    return "\n".join(out) + "\n"
+
+
+def summarize_mfma_busy(csv_path, xcds=8, simds=1024):
+    """Summary of one rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES,
+    SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE over the score kernel's dispatches:
+    the matrix-pipe busy fraction per SIMD against the GPU-busy cycles
+    (GRBM_GUI_ACTIVE is summed over the XCDs)."""
+    with open(csv_path) as f:
+        rows = [r for r in csv.DictReader(f) if "score_bf16_kernel" in r["Kernel_Name"]]
+    agg = {}
+    ns = 0.0
+    seen = set()
+    for r in rows:
+        agg[r["Counter_Name"]] = agg.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r["Dispatch_Id"] not in seen:
+            seen.add(r["Dispatch_Id"])
+            ns += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    busy = agg["SQ_VALU_MFMA_BUSY_CYCLES"]
+    gpu = agg["GRBM_GUI_ACTIVE"] / xcds
+    out = ["dispatches: %d" % len(seen),
+           "kernel_ns_total: %.0f" % ns,
+           "sq_valu_mfma_busy_cycles: %.6g" % busy,
+           "grbm_gui_active_per_xcd: %.6g" % gpu,
+           "mfma_busy_per_simd: %.6g" % (busy / simds),
+           "mfma_busy_fraction: %.4f" % (busy / simds / gpu)]
+    if "SQ_BUSY_CYCLES" in agg:
+        out.append("sq_busy_cycles: %.6g" % agg["SQ_BUSY_CYCLES"])
     return "\n".join(out) + "\n"
 
 
@@ -130,6 +170,33 @@ def make_inputs(cfg_n, dev):
         q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=cfg_n, device=dev)
         dist = "q,kc ~ N(0,1)/sqrt(D_I), w ~ N(0,1)/sqrt(H_I)"
     return c, q, w, kc, dist
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def select_algorithmic_bytes(S, T, m, k, chunk):
+    """Bytes the select stage must move for one call: the chunk scores read
+    once (4 B per pair), the outputs written once (8 B per entry), and with
+    several chunks the running lists read and written once per extra chunk
+    (16 B per entry)."""
+    i = np.arange(S, dtype=np.int64)
+    n = np.minimum(T, (i + 1) // m)
+    n_max = int(n.max()) if S else 0
+    n_round = (n_max + 255) // 256 * 256
+    c = chunk or (n_round if n_round <= 65536 else 65536)
+    c = max(min(c, n_round), 1)
+    extra = np.maximum((n + c - 1) // c - 1, 0)
+    lists = 16 * k * int(extra.sum())
+    return 4 * int(n.sum()) + 8 * S * k + lists
 
 
 def cpu_baseline(q, w, kc, m, k, S, T, target_s, max_rows, seed):
@@ -161,6 +228,7 @@ def cpu_baseline(q, w, kc, m, k, S, T, target_s, max_rows, seed):
         "value": pairs / dt,
         "unit": "pairs/s",
         "cores": threads,
+        "cpu": cpu_model(),
         "kind": "oracle",
         "sample": "%d query rows of the same workload (boundary rows plus seeded uniform draws), "
                   "%d valid pairs, %.2f s wall on %d host threads" % (len(rows), pairs, dt, threads),
@@ -332,8 +400,14 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs "
                          "(needs --copy-probe with the probe size those runs used); no GPU")
+    ap.add_argument("--mfma-busy-from", metavar="PMC_CSV",
+                    help="print the MFMA-busy summary of a rocprofv3 --pmc run with "
+                         "SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE; no GPU")
     args = ap.parse_args()
 
+    if args.mfma_busy_from:
+        sys.stdout.write(summarize_mfma_busy(args.mfma_busy_from))
+        return
     if args.traffic_from:
         if not args.copy_probe:
             raise SystemExit("--traffic-from needs --copy-probe BYTES")
@@ -360,6 +434,7 @@ def main():
 
     torch.cuda.reset_peak_memory_stats(dev)
     base_alloc = torch.cuda.memory_allocated(dev)
+    free_before = torch.cuda.mem_get_info(dev)[0]
     c, q, w, kc, dist = make_inputs(args.workload, dev)
     S, T, H, D, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
     torch.cuda.synchronize()
@@ -404,6 +479,9 @@ def main():
     resident = (q.numel() * q.element_size() + w.numel() * w.element_size()
                 + kc.numel() * kc.element_size() + idx.numel() * 4 + score.numel() * 4)
     peak = torch.cuda.max_memory_allocated(dev) - base_alloc
+    # Device memory taken since the start (hipMemGetInfo): torch's reserved
+    # pool; the library itself allocates nothing.
+    device_used = free_before - torch.cuda.mem_get_info(dev)[0]
     ms = (t1 - t0) * 1e3 / args.steps
     P = pair_count(S, T, m)
     flops = P * 2 * H * D
@@ -416,6 +494,11 @@ def main():
     traffic = None
     if args.workload == 3 and not (args.chunk or args.tile or args.budget):
         traffic = read_traffic()
+    sel_launches = sel_n / args.steps
+    sel_bytes = select_algorithmic_bytes(S, T, m, k, args.chunk) / max(sel_launches, 1)
+    sel_launch_ms = sel_ms / max(sel_n, 1)
+    sel_gbs = sel_bytes / (sel_launch_ms * 1e-3) / 1e9 if sel_n else 0.0
+    sel_traffic = traffic["select"] if traffic else None
 
     out = {
         "metric": METRIC,
@@ -451,6 +534,19 @@ def main():
             "launches_per_step": score_n / args.steps,
             "flops_per_launch": flops_per_launch,
         },
+        "select_roofline": {
+            "bound": "hbm",
+            "achieved": sel_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": sel_gbs / HBM_PEAK_GBS,
+            "traffic": sum(sel_traffic) if sel_traffic else None,
+            "traffic_fetch_write": list(sel_traffic) if sel_traffic else None,
+            "kernel": "select_kernel",
+            "launch_ms": sel_launch_ms,
+            "launches_per_step": sel_launches,
+            "bytes_per_launch": sel_bytes,
+        },
         "mfma_util_pct": 100.0 * flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
         "kernel_ms_per_step": {"score": score_ms / args.steps, "select": sel_ms / args.steps,
                                "merge": prof["merge"][0] / args.steps},
@@ -459,6 +555,7 @@ def main():
                      "resident_inputs_outputs_gib": resident / 2 ** 30,
                      "above_resident_gib": (peak - resident) / 2 ** 30,
                      "input_generation_peak_gib": gen_peak / 2 ** 30,
+                     "device_memory_taken_gib": device_used / 2 ** 30,
                      "avoided_fp32_score_tensor_gib": S * H * T * 4 / 2 ** 30},
     }
 
@@ -467,6 +564,8 @@ def main():
                                                  args.cpu_max_rows, args.workload)
         out["cpu_baseline"] = {kk: base[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
         out["cpu_baseline"]["extrapolated_full_s"] = base["extrapolated_full_s"]
+        out["cpu_baseline"]["cpu"] = base["cpu"]
+        out["cpu_baseline"]["gpu_over_cpu"] = out["value"] / base["value"]
         rt = torch.from_numpy(rows).to(dev)
         g_idx = idx[rt].cpu().numpy()
         n = np.minimum(T, (rows + 1) // m)

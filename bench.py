@@ -52,11 +52,15 @@ def pair_count(S, T, m, q_pos0=0):
 
 
 def source_hash(sources=SCORE_SOURCES):
-    """sha256 over the sources that define a kernel."""
+    """sha256 over the code of the sources that define a kernel (// comments
+    and whitespace removed, so that comment edits keep the counters valid)."""
+    import re
     h = hashlib.sha256()
     for rel in sources:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        code = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(code.split()).encode())
     return h.hexdigest()
 
 

@@ -10,7 +10,9 @@
 // writes the pass's [R, C] head-reduced scores, then the select kernel folds
 // them into each row's running best-k list; the last chunk's select pass sorts
 // the lists and writes idx/score.  Scratch is R*(4C + 16 [+ 8k + 16]) bytes,
-// set by the workspace and never by S*T.
+// set by the workspace and never by S*T.  Problems with few query rows cut
+// one chunk into G key splits instead, run in parallel, each with its own
+// list, and merge the G lists pairwise (R*(4C + G*(16 + 8k + 16)) bytes).
 #include <stdint.h>
 #include <string.h>
 

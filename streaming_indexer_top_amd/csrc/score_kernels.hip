@@ -13,13 +13,17 @@
 //
 // bf16 path: the contraction over the head dimension is a dense GEMM
 // [H_I, D_I] x [D_I, N] per query, run on the MFMA units with
-// v_mfma_f32_16x16x32_bf16 (fp32 accumulation).  A workgroup holds 8 query
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulation).  A workgroup holds 8 query
 // rows, one per wave; each wave keeps its query's q fragments (64 heads x 128
 // dims = 64 VGPRs) and head weights resident and streams key tiles of NT keys
-// that the whole workgroup stages, double-buffered, through LDS.  In the
-// 16x16 accumulator layout a lane owns one key column and 4 heads per 16-head
-// block, so the ReLU and the weighted head sum run in registers, with two
-// cross-lane adds at the end.
+// that the whole workgroup brings into LDS (by LDS DMA, double-buffered).  In
+// the 32x32 accumulator layout a lane owns one key column and 16 rows of each
+// 32-head block, so the ReLU and the weighted head sum run in registers, with
+// one cross-half swap at the end.  A second grid dimension can split the
+// chunk's keys (few query rows, e.g. decoding); the kernel details are at
+// score_bf16_kernel below.
+//
+// fp32 path: one thread per key, plain fp32 FMA (correctness path).
 #include "csa_internal.h"
 
 namespace csa {

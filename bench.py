@@ -363,8 +363,36 @@ def run_decode(args, dev):
         same = bool(torch.equal(ref[0], out[0])) and bool(
             torch.equal(ref[1].view(torch.int32), out[1].view(torch.int32)))
         ms = (t1 - t0) * 1e3 / args.steps
+        graph_ms = None
+        if args.graph:
+            # The same call captured once in a HIP graph and replayed: no
+            # per-launch host overhead (the library enqueues only kernels).
+            ws_bytes = csa.workspace_size(R, T, H, D, m, k, q_pos0=q_pos0, key_splits=splits)
+            ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+            gi = torch.empty((R, k), dtype=torch.int32, device=dev)
+            gs = torch.empty((R, k), dtype=torch.float32, device=dev)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                csa.topk(q, w, kc, m, k, workspace=ws, out=(gi, gs), **kw)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                csa.topk(q, w, kc, m, k, workspace=ws, out=(gi, gs), **kw)
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                g.replay()
+            torch.cuda.synchronize()
+            graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+            same = same and bool(torch.equal(ref[0], gi)) and bool(
+                torch.equal(ref[1].view(torch.int32), gs.view(torch.int32)))
         print(json.dumps({
             "mode": "decode", "plan": "key splits (auto)" if splits == 0 else "chunks only",
+            "graph_replay_ms": graph_ms,
             "rows": R, "T": T, "k": k, "q_pos0": q_pos0, "ms_per_call": ms,
             "pairs_per_s": P / (ms * 1e-3),
             "mfma_util_pct": 100.0 * P * 2 * H * D / (ms * 1e-3) / (MFMA_BUSY_PEAK * 1e12),
@@ -395,6 +423,8 @@ def main():
     ap.add_argument("--decode", type=int, default=0,
                     help="time this many new queries at the end of the workload's sequence "
                          "(decode shape) with and without key splits")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode: also time replays of the call captured in a HIP graph")
     ap.add_argument("--batch", type=int, default=0,
                     help="time one batched call over this many independent problems of the "
                          "workload's shape (one JSON line)")

@@ -360,6 +360,44 @@ def test_random_configs_bf16_gaussian(case):
     assert_no_fail(fails)
 
 
+@pytest.mark.parametrize("shape", ["chunks", "key_splits"])
+def test_hip_graph_replays_match_eager(shape):
+    """The call enqueues only kernel launches on the caller's stream (no
+    allocation, no memset), so it can be captured in a HIP graph.  Every
+    replay, with eager work in between, equals the eager result."""
+    if shape == "chunks":
+        S, T, H, D, m, k, q_pos0, kw = 3000, 2500, 64, 128, 4, 512, 0, dict(chunk_keys=256)
+    else:
+        S, T, H, D, m, k, q_pos0, kw = 16, 60000, 64, 128, 1, 2048, 59984, {}
+    q, w, kc = [t.to(DEV) for t in inputs.bf16_gaussian(S, T, H, D, seed=70)]
+    ws_bytes = csa.workspace_size(S, T, H, D, m, k, q_pos0=q_pos0, **kw)
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=DEV)
+    idx = torch.empty((S, k), dtype=torch.int32, device=DEV)
+    sc = torch.empty((S, k), dtype=torch.float32, device=DEV)
+    e_idx, e_sc = csa.topk(q, w, kc, m, k, q_pos0=q_pos0, **kw)  # eager (also warms up)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        csa.topk(q, w, kc, m, k, q_pos0=q_pos0, workspace=ws, out=(idx, sc), **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        csa.topk(q, w, kc, m, k, q_pos0=q_pos0, workspace=ws, out=(idx, sc), **kw)
+    for rep in range(3):
+        idx.fill_(7)
+        sc.zero_()
+        ws.fill_(0xAB)  # the replay must not depend on the workspace's contents
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, e_idx), "replay %d" % rep
+        assert torch.equal(sc.view(torch.int32), e_sc.view(torch.int32)), "replay %d" % rep
+        _ = (q.float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_small_workspace_many_passes():
     S, T, H, D, m, k = 2000, 500, 8, 64, 4, 64
     q, w, kc = inputs.integer_valued(S, T, H, D, seed=6, dtype=torch.bfloat16, signed_w=True)

@@ -84,7 +84,8 @@ extern "C" {
  */
 typedef struct csa_opts {
     /* Keys per partition chunk: each query keeps its best k of every chunk
-     * and merges them into a running list.  A multiple of 256, or 0. */
+     * and merges them into a running list.  A multiple of 256 up to 2^24, or
+     * 0. */
     int64_t chunk_keys;
     /* Keys staged in LDS per step of the score kernel: 64, 128, 256, or 0. */
     int32_t key_tile;

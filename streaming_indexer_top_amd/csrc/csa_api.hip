@@ -28,6 +28,8 @@ constexpr int64_t kDefaultBudget = int64_t(2) << 30;
 constexpr int64_t kDefaultChunkCap = 65536;  // single chunk up to this many keys
 constexpr int64_t kDefaultChunk = 65536;
 constexpr int32_t kDefaultTile = 128;
+constexpr int64_t kMaxChunk = int64_t(1) << 24;  // keys; chunk offsets stay 32-bit in the kernels
+constexpr int64_t kMaxRowsNoKeys = int64_t(1) << 20;  // rows per pass when no row has a key
 constexpr size_t kAlign = 256;
 // Key splits (automatic): used when a problem has fewer query blocks than
 // this (a 256-CU part then has idle CUs), doubled until blocks x splits
@@ -83,7 +85,8 @@ int check_args(int64_t S, int64_t T, int32_t H, int32_t D, int32_t m, int64_t k,
     if (T > (int64_t)INT32_MAX - 1) return CSA_ERR_UNSUPPORTED;
     if (S > ((int64_t)1 << 40) || q_pos0 > ((int64_t)1 << 40)) return CSA_ERR_UNSUPPORTED;
     if (opts) {
-        if (opts->chunk_keys < 0 || (opts->chunk_keys % 256) != 0) return CSA_ERR_BAD_OPTION;
+        if (opts->chunk_keys < 0 || (opts->chunk_keys % 256) != 0 || opts->chunk_keys > kMaxChunk)
+            return CSA_ERR_BAD_OPTION;
         if (opts->key_tile != 0 && opts->key_tile != 64 && opts->key_tile != 128 &&
             opts->key_tile != 256)
             return CSA_ERR_BAD_OPTION;
@@ -221,7 +224,7 @@ const char *csa_status_str(int status)
     case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small for one query block";
     case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 4096 or T >= 2^31)";
     case CSA_ERR_HIP: return "HIP call or kernel launch failed";
-    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256, key_tile one of 64/128/256, key_splits 0 or a power of two up to 64, reserved fields 0";
+    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256 up to 2^24, key_tile one of 64/128/256, key_splits 0 or a power of two up to 64, reserved fields 0";
     default: return "unknown status";
     }
 }
@@ -281,6 +284,7 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
 {
     int st = CSA_OK;
     if (S == 0) return CSA_OK;
+    if (p.chunk == 0 && rows > kMaxRowsNoKeys) rows = kMaxRowsNoKeys;  // padding-only passes
     if (p.chunk > 0) {
         if (rows < S && p.splits == 1) {
             // Several passes.  Score workgroups of one pass run in rounds of

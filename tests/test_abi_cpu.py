@@ -147,7 +147,8 @@ def test_workspace_too_small():
 
 def test_bad_options():
     lib = csa.load_library()
-    for field, val in (("chunk_keys", 100), ("key_tile", 96), ("workspace_budget", -1),
+    for field, val in (("chunk_keys", 100), ("chunk_keys", (1 << 24) + 256), ("key_tile", 96),
+                       ("workspace_budget", -1),
                        ("key_splits", 3), ("key_splits", 128), ("key_splits", -2)):
         o = binding.csa_opts()
         setattr(o, field, val)

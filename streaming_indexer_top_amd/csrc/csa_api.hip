@@ -377,7 +377,11 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
             se.emit = c == nch - 1 && p.splits == 1;
             st = launch_timed(CSA_KERNEL_SELECT, s, [&] { return csa::launch_select(se, s); });
             if (st != CSA_OK) return st;
-            for (int64_t half = p.splits / 2; half >= 1; half /= 2) {
+            // Merge rounds: four lists into one while at least four are left
+            // (k <= 2048), else two into one.
+            for (int64_t left = p.splits; left > 1;) {
+                const bool four = left >= 4 && k <= 2048;
+                const int64_t next = four ? left / 4 : left / 2;
                 csa::MergeArgs mg;
                 mg.lists = lists;
                 mg.state = state;
@@ -386,10 +390,12 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
                 mg.row0 = r0;
                 mg.rows = nr;
                 mg.k = k;
-                mg.half = (int32_t)half;
-                mg.emit = half == 1;
+                mg.half = (int32_t)next;
+                mg.four = four;
+                mg.emit = next == 1;
                 st = launch_timed(CSA_KERNEL_MERGE, s, [&] { return csa::launch_merge(mg, s); });
                 if (st != CSA_OK) return st;
+                left = next;
             }
         }
     }

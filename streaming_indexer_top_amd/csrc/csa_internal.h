@@ -90,8 +90,9 @@ struct SelectArgs {
 };
 
 // One round of the merge of split lists: for p < half, the lists of virtual
-// rows p*rows + r and (p+half)*rows + r are merged into the first; with
-// emit (half == 1) the merged best k are written as the row's outputs.
+// rows p*rows + r and (p+half)*rows + r are merged into the first (with
+// `four`, k <= 2048 only: the lists p + j*half, j = 0..3); with emit (the
+// last round) the merged best k are written as the row's outputs.
 struct MergeArgs {
     uint64_t *lists;      // [splits*rows][k]
     RowState *state;      // [splits*rows]
@@ -100,6 +101,7 @@ struct MergeArgs {
     int64_t row0, rows, k;
     int32_t half;
     int32_t emit;
+    int32_t four;
 };
 
 // Dtype codes as in the public header.

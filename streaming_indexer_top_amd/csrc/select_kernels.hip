@@ -897,6 +897,56 @@ __global__ __launch_bounds__(NT) void merge_kernel(MergeArgs a)
     }
 }
 
+// A four-way merge round (k <= 2048): workgroup (p, rl) merges the lists of
+// virtual rows (p + j*quarter)*rows + rl, j = 0..3, into the first.  The best
+// k of the union is the best k of (best k of lists 0,1) u (best k of 2,3).
+__global__ __launch_bounds__(NT) void merge4_kernel(MergeArgs a)
+{
+    constexpr int K = 2048;
+    extern __shared__ uint64_t smem[];
+    const int tid = threadIdx.x;
+    const int k = (int)a.k;
+    const int64_t q4 = a.half;  // quarter: lists p, p+q4, p+2*q4, p+3*q4
+    const int64_t p = (int64_t)blockIdx.x / a.rows;
+    const int64_t rl = a.rows - 1 - ((int64_t)blockIdx.x - p * a.rows);
+    int64_t v[4];
+    int n[4];
+    uint64_t *l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = (p + j * q4) * a.rows + rl;
+        n[j] = a.state[v[j]].count;
+        l[j] = smem + j * K;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        for (int e = tid; e < n[j]; e += NT) l[j][e] = a.lists[v[j] * a.k + e];
+    __syncthreads();
+    constexpr int PT = Caps<K>::PT;
+    const int p0 = tid * PT;
+    uint64_t ab[PT], cd[PT], kth = 0;
+    const int nab = min(k, n[0] + n[1]), ncd = min(k, n[2] + n[3]);
+    const int oab = merge_share<PT>(l[0], n[0], l[1], n[1], nab, p0, -1, ab, kth);
+    const int ocd = merge_share<PT>(l[2], n[2], l[3], n[3], ncd, p0, -1, cd, kth);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+        if (t < oab) l[0][p0 + t] = ab[t];
+        if (t < ocd) l[2][p0 + t] = cd[t];
+    }
+    __syncthreads();
+    const int total = min(k, nab + ncd);
+    uint64_t outv[PT];
+    const int nout = merge_share<PT>(l[0], nab, l[2], ncd, total, p0, -1, outv, kth);
+    if (a.emit) {
+        const int64_t row = a.row0 + rl;
+        emit_share<PT>(a.out_idx + row * a.k, a.out_score + row * a.k, k, p0, outv, nout);
+    } else {
+        store_share<PT>(a.lists + v[0] * a.k, k, p0, outv, nout);
+        if (tid == 0) a.state[v[0]].count = total;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream)
@@ -904,7 +954,19 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t stream)
     if (a.rows <= 0 || a.half <= 0) return hipSuccess;
     const dim3 grid((unsigned)(a.rows * a.half));
     if (a.k <= 2048) {
-        merge_kernel<2048><<<grid, dim3(NT), 2 * 2048 * sizeof(uint64_t), stream>>>(a);
+        if (a.four) {
+            static bool attr_set = false;  // benign race: every caller sets the same value
+            if (!attr_set) {
+                const hipError_t e = hipFuncSetAttribute((const void *)merge4_kernel,
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         4 * 2048 * (int)sizeof(uint64_t));
+                if (e != hipSuccess) return e;
+                attr_set = true;
+            }
+            merge4_kernel<<<grid, dim3(NT), 4 * 2048 * sizeof(uint64_t), stream>>>(a);
+        } else {
+            merge_kernel<2048><<<grid, dim3(NT), 2 * 2048 * sizeof(uint64_t), stream>>>(a);
+        }
     } else {
         merge_kernel<4096><<<grid, dim3(NT), 2 * 4096 * sizeof(uint64_t), stream>>>(a);
     }

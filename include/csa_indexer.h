@@ -92,9 +92,10 @@ typedef struct csa_opts {
     /* Key splits (bf16 only, ignored when chunk_keys is set): the usable keys
      * form one chunk cut into this many splits that are scored and selected
      * in parallel, each split's best k going to its own list, and the lists
-     * are merged pairwise.  For problems with few query rows (decoding a few
-     * new queries against a long key cache), where chunks alone would leave
-     * most of the GPU idle.  0 = automatic (used for fewer than 2048 rows
+     * are merged in rounds that combine four lists (k <= 2048) or two.
+     * For problems with few query rows (decoding a few new queries against
+     * a long key cache), where chunks alone would leave most of the GPU
+     * idle.  0 = automatic (used for fewer than 2048 rows
      * when one pass fits the workspace budget), 1 = never, or a power of two
      * up to 64. */
     int32_t key_splits;

@@ -26,7 +26,8 @@ def device_asm(src, tmp_path):
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I" + os.path.join(ROOT, "include"), "-S", "--cuda-device-only",
            os.path.join(CSRC, src), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    # hipcc leaves intermediate files in its working directory.
+    subprocess.run(cmd, check=True, capture_output=True, text=True, cwd=str(tmp_path))
     return out.read_text()
 
 

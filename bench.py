@@ -136,13 +136,16 @@ def summarize_counters(fetch_csv, write_csv, copy_bytes):
     return "\n".join(out) + "\n"
 
 
-def summarize_mfma_busy(csv_path, xcds=8, simds=1024):
+def summarize_mfma_busy(csv_path, match="score_bf16_kernel", xcds=8, simds=1024):
     """Summary of one rocprofv3 --pmc run with SQ_VALU_MFMA_BUSY_CYCLES,
-    SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE over the score kernel's dispatches:
-    the matrix-pipe busy fraction per SIMD against the GPU-busy cycles
-    (GRBM_GUI_ACTIVE is summed over the XCDs)."""
+    SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE over the dispatches of the kernels
+    whose name contains `match` (default: the score kernel): the matrix-pipe
+    busy fraction per SIMD against the GPU-busy cycles (GRBM_GUI_ACTIVE is
+    summed over the XCDs), and the shader clock those cycles imply."""
     with open(csv_path) as f:
-        rows = [r for r in csv.DictReader(f) if "score_bf16_kernel" in r["Kernel_Name"]]
+        rows = [r for r in csv.DictReader(f) if match in r["Kernel_Name"]]
+    if not rows:
+        raise SystemExit("%s: no dispatch of a kernel matching %r" % (csv_path, match))
     agg = {}
     ns = 0.0
     seen = set()
@@ -158,7 +161,8 @@ def summarize_mfma_busy(csv_path, xcds=8, simds=1024):
            "sq_valu_mfma_busy_cycles: %.6g" % busy,
            "grbm_gui_active_per_xcd: %.6g" % gpu,
            "mfma_busy_per_simd: %.6g" % (busy / simds),
-           "mfma_busy_fraction: %.4f" % (busy / simds / gpu)]
+           "mfma_busy_fraction: %.4f" % (busy / simds / gpu),
+           "shader_clock_ghz: %.3f" % (gpu / ns)]
     if "SQ_BUSY_CYCLES" in agg:
         out.append("sq_busy_cycles: %.6g" % agg["SQ_BUSY_CYCLES"])
     return "\n".join(out) + "\n"
@@ -401,6 +405,32 @@ def run_decode(args, dev):
             "bit_identical_to_auto": same}), flush=True)
 
 
+def run_gemm_probe(args, dev):
+    """A square bf16 GEMM through torch.matmul (the vendor GEMM library), timed
+    with CUDA events on torch's stream: what a tuned dense contraction
+    sustains on this chip under the same power limit, for comparison with the
+    score kernel's fraction of the nominal peak."""
+    n = args.gemm_probe
+    g = torch.Generator(device=dev).manual_seed(0)
+    a = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev).to(torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(max(args.warmup, 1)):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        torch.matmul(a, b, out=c)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"probe": "gemm_bf16", "n": n, "steps": args.steps, "ms_per_gemm": ms,
+                      "tflops": tflops, "frac_of_2500": tflops / 2500.0}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,10 +467,15 @@ def main():
     ap.add_argument("--mfma-busy-from", metavar="PMC_CSV",
                     help="print the MFMA-busy summary of a rocprofv3 --pmc run with "
                          "SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE; no GPU")
+    ap.add_argument("--kernel-match", default="score_bf16_kernel",
+                    help="with --mfma-busy-from: summarize the kernels whose name contains this")
+    ap.add_argument("--gemm-probe", type=int, default=0,
+                    help="time a plain library bf16 GEMM (torch.matmul, N x N x N) as a "
+                         "reference for the MFMA rate this chip sustains; one JSON line")
     args = ap.parse_args()
 
     if args.mfma_busy_from:
-        sys.stdout.write(summarize_mfma_busy(args.mfma_busy_from))
+        sys.stdout.write(summarize_mfma_busy(args.mfma_busy_from, args.kernel_match))
         return
     if args.traffic_from:
         if not args.copy_probe:
@@ -458,6 +493,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.gemm_probe:
+        run_gemm_probe(args, dev)
+        return
     csa.load_library()
     if args.batch:
         run_batched(args, dev)

@@ -165,6 +165,18 @@ def summarize_mfma_busy(csv_path, match="score_bf16_kernel", xcds=8, simds=1024)
            "shader_clock_ghz: %.3f" % (gpu / ns)]
     if "SQ_BUSY_CYCLES" in agg:
         out.append("sq_busy_cycles: %.6g" % agg["SQ_BUSY_CYCLES"])
+    cus = simds // 4
+    if "SQ_ACTIVE_INST_VALU" in agg:
+        # rocprofiler's VALUBusy for gfx9: quad-cycles summed over the SIMDs,
+        # per CU, against the GPU-busy cycles.
+        out.append("valu_busy_fraction: %.4f" % (agg["SQ_ACTIVE_INST_VALU"] / cus / gpu))
+    for name in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_WAVES"):
+        if name in agg:
+            out.append("%s: %.6g" % (name.lower(), agg[name]))
+    if "SQ_INSTS_VALU" in agg and agg.get("SQ_INSTS_MFMA"):
+        # SQ_INSTS_VALU counts the MFMAs too.
+        out.append("non_mfma_valu_per_mfma: %.3f"
+                   % ((agg["SQ_INSTS_VALU"] - agg["SQ_INSTS_MFMA"]) / agg["SQ_INSTS_MFMA"]))
     return "\n".join(out) + "\n"
 
 
@@ -539,12 +551,18 @@ def main():
     csa.profile_collect()  # drop anything recorded so far
 
     csa.profile_enable(True)
+    # One event between consecutive calls on the call stream: per-call times
+    # without a synchronisation inside the timed region.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         csa.topk(q, w, kc, m, k, **kw)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    call_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     csa.profile_enable(False)
     prof = csa.profile_collect()
 
@@ -619,6 +637,9 @@ def main():
             "launches_per_step": sel_launches,
             "bytes_per_launch": sel_bytes,
         },
+        "call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0],
+                    "max": call_ms[-1]},
+        "pairs_per_s_median_call": P / (call_ms[len(call_ms) // 2] * 1e-3),
         "mfma_util_pct": 100.0 * flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
         "kernel_ms_per_step": {"score": score_ms / args.steps, "select": sel_ms / args.steps,
                                "merge": prof["merge"][0] / args.steps},

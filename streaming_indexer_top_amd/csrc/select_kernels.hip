@@ -505,15 +505,29 @@ __device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_e
         sh.nB = 0u;
     }
     __syncthreads();
+    // Without a floor every key in range is eligible (also -inf and NaN, which
+    // then fail both thresholds or pass f_edge = -inf exactly as compared).
+    const bool nofilt = !r.filt;
+    // Each lane's slot for the keys it drops: the bucket words behind the
+    // candidate regions are unused until the sort, and one slot per lane keeps
+    // the stores of a wave free of same-address conflicts.
+    const uint32_t dummy = (uint32_t)Caps<K>::Cand + (uint32_t)tid;
     auto process = [&](const float (&v)[V], int64_t base) {
+        // Classification without branches: 2 bits per key (1 = region A,
+        // 2 = region B, 0 = dropped) and the two counts packed in one word.
+        const int64_t rem64 = r.len - base;
+        const int rem = rem64 <= 0 ? 0 : (rem64 >= V ? V : (int)rem64);
         uint32_t cls = 0, cnt = 0;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const float x = v[i];
-            const bool ok = base + i < r.len && (!r.filt || x > r.f_floor);
-            const uint32_t c = !ok ? 0u : (x >= f_sure ? 1u : (x >= f_edge ? 2u : 0u));
-            cls |= c << (2 * i);
-            cnt += c == 1u ? 1u : (c == 2u ? 0x10000u : 0u);
+            const bool ok = (i < rem) & (nofilt | (x > r.f_floor));
+            const bool ge_s = x >= f_sure;
+            const bool isA = ok & ge_s;
+            const bool isB = ok & !ge_s & (x >= f_edge);
+            cls |= (isA ? 1u : 0u) << (2 * i);
+            cls |= (isB ? 2u : 0u) << (2 * i);
+            cnt += (isA ? 1u : 0u) + (isB ? 0x10000u : 0u);
         }
         const uint32_t incl = wave_incl_sum(cnt);
         const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
@@ -523,22 +537,27 @@ __device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_e
             if (tot & 0xFFFFu) ba = atomicAdd(&sh.nA, tot & 0xFFFFu);
             if (tot >> 16) bb = atomicAdd(&sh.nB, tot >> 16);
         }
+        ba = (uint32_t)__builtin_amdgcn_readfirstlane((int)ba);
+        bb = (uint32_t)__builtin_amdgcn_readfirstlane((int)bb);
         const uint32_t excl = incl - cnt;
-        uint32_t pa = (uint32_t)__builtin_amdgcn_readfirstlane((int)ba) + (excl & 0xFFFFu);
-        uint32_t pb = (uint32_t)__builtin_amdgcn_readfirstlane((int)bb) + (excl >> 16);
+        uint32_t pa = ba + (excl & 0xFFFFu);
+        uint32_t pb = (uint32_t)kCapA + bb + (excl >> 16);
+        // The counts stay within the capacities on every path that calls
+        // this; a wave whose slots would not fit stores only what fits.
+        const bool fits = ba + (tot & 0xFFFFu) <= (uint32_t)kCapA &&
+                          bb + (tot >> 16) <= (uint32_t)kCapB;  // wave-uniform
+        const uint32_t capA = fits ? 0xFFFFFFFFu : (uint32_t)kCapA;
+        const uint32_t capB = fits ? 0xFFFFFFFFu : (uint32_t)(kCapA + kCapB);
+        // Every key is stored, a dropped one to this lane's spare slot.
+        const uint32_t j0 = r.c0 + (uint32_t)base;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const uint32_t c = (cls >> (2 * i)) & 3u;
-            if (c != 0u) {
-                const uint64_t key = make_key(v[i], r.c0 + (uint32_t)(base + i));
-                if (c == 1u) {
-                    if (pa < (uint32_t)kCapA) cand[pa] = key;
-                    ++pa;
-                } else {
-                    if (pb < (uint32_t)kCapB) cand[kCapA + pb] = key;
-                    ++pb;
-                }
-            }
+            const bool isA = c == 1u, isB = c == 2u;
+            const uint32_t slot = (isA & (pa < capA)) ? pa : ((isB & (pb < capB)) ? pb : dummy);
+            pa += isA ? 1u : 0u;
+            pb += isB ? 1u : 0u;
+            cand[slot] = make_key(v[i], j0 + (uint32_t)i);
         }
     };
     // Three buffers rotate by name (the loop is unrolled by three): a copy

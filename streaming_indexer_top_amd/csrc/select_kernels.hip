@@ -299,10 +299,11 @@ __device__ void bitonic_desc(uint64_t *cand, int n, int tid)
 // together, descending, into cand[0..nA+nB).  Every A key must be larger
 // than every B key (A = above the boundary, B = in it; either may be empty).
 //
-// Bucket sort with the keys held in registers: each region's score range
-// [min, max] is cut into buckets of equal width in score value (B gets a
-// share of the buckets proportional to its size, A the rest), which
-// is monotone, so bucket order is key order.  One LDS atomic per key counts
+// Bucket sort with the keys held in registers: each region's range
+// [min, max] is cut into buckets of equal width (in the orderable integer
+// when the region's scores share one sign, else in score value; B gets a
+// share of the buckets proportional to its size, A the rest), which is
+// monotone, so bucket order is key order.  One LDS atomic per key counts
 // its bucket and gives its slot there; a prefix sum over the buckets (from the
 // top) gives each bucket's first position; keys are scattered into bucket
 // order, and each then finds its place inside its bucket by counting the
@@ -365,15 +366,26 @@ __device__ __forceinline__ void sort_keys(uint64_t *cand, int nA, int nB, uint32
         nbB = nbB < 1 ? 1 : (nbB > kBuckets - 1 && nA > 0 ? kBuckets - 1 : nbB);
     }
     const int nbA = kBuckets - nbB;
-    const float fAlo = score_of_orderable(loA), fAhi = score_of_orderable(hiA);
-    const float fBlo = score_of_orderable(loB), fBhi = score_of_orderable(hiB);
-    const float scA = fAhi > fAlo ? (float)nbA / (fAhi - fAlo) : 0.0f;
-    const float scB = fBhi > fBlo ? (float)nbB / (fBhi - fBlo) : 0.0f;
-    // Bucket of a key: monotone in its score (clamps also catch inf/NaN).
-    auto bucket = [&](uint64_t kk, bool inA) -> uint32_t {
-        const float x = score_of_orderable((uint32_t)(kk >> 32));
-        float t = inA ? (x - fAlo) * scA : (x - fBlo) * scB;
-        t = fminf(fmaxf(t, 0.0f), (float)((inA ? nbA : nbB) - 1));
+    // Bucket of a key, monotone in it.  A region whose scores share one sign
+    // is cut evenly in the orderable integer, which is close to a log scale
+    // and gives the dense low end of a score tail finer buckets; a region
+    // that crosses zero is cut evenly in score value (in the integer it
+    // would spend most buckets on tiny magnitudes).  Either map is monotone,
+    // so bucket order is key order; the clamps also catch inf and NaN.
+    const bool intA = (loA ^ hiA) < 0x80000000u, intB = (loB ^ hiB) < 0x80000000u;
+    const float fAlo = intA ? 0.0f : score_of_orderable(loA);
+    const float fBlo = intB ? 0.0f : score_of_orderable(loB);
+    const float wA = intA ? (float)(hiA - loA) : score_of_orderable(hiA) - fAlo;
+    const float wB = intB ? (float)(hiB - loB) : score_of_orderable(hiB) - fBlo;
+    const float scA = wA > 0.0f ? (float)nbA / wA : 0.0f;
+    const float scB = wB > 0.0f ? (float)nbB / wB : 0.0f;
+    const float topA = (float)(nbA - 1), topB = (float)(nbB - 1);
+    auto bucket_of = [&](uint64_t kk, bool inA) -> uint32_t {
+        const uint32_t u = (uint32_t)(kk >> 32);
+        const bool in_int = inA ? intA : intB;
+        const float x = in_int ? (float)(u - (inA ? loA : loB)) : score_of_orderable(u);
+        float t = (x - (inA ? fAlo : fBlo)) * (inA ? scA : scB);
+        t = fminf(fmaxf(t, 0.0f), inA ? topA : topB);
         return (uint32_t)(int)t + (inA ? (uint32_t)nbB : 0u);
     };
     uint32_t bkt[PT], slot[PT];
@@ -384,7 +396,7 @@ __device__ __forceinline__ void sort_keys(uint64_t *cand, int nA, int nB, uint32
         bkt[i] = 0u;
         slot[i] = 0u;
         if (e < (inA ? nA : nB)) {
-            bkt[i] = bucket(key[i], inA);
+            bkt[i] = bucket_of(key[i], inA);
             slot[i] = atomicAdd(&bk[bkt[i]], 1u);
         }
     }

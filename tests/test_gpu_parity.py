@@ -148,6 +148,39 @@ def test_signed_zero_scores_are_positive():
     assert not np.any(np.signbit(g_sc[g_idx >= 0]))
 
 
+@pytest.mark.parametrize("sign", ["negative", "positive"])
+@pytest.mark.parametrize("k", [256, 2048])
+def test_one_sign_scores_bf16(sign, k):
+    """All weights of one sign: every score has that sign (or is zero), so
+    the sort's regions lie on one side of zero and are bucketed in the
+    orderable integer; negative rows also put the best keys nearest zero.
+    All rows checked by the tolerance rules."""
+    S, T, H, D, m = 4096, 3000, 64, 128, 1
+    q, w, kc = inputs.bf16_gaussian(S, T, H, D, seed=70 + k)
+    w = w.abs() if sign == "positive" else -w.abs()
+    say("one-sign scores %s k=%d" % (sign, k))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k)
+    fails, stats = checks.check_float(g_idx, g_sc, o_idx, o_sc, q.float().numpy(),
+                                      w.float().numpy(), kc.float().numpy(), np.arange(S),
+                                      T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
+@pytest.mark.parametrize("chunk", [0, 1024])
+def test_negative_weights_integer_bit_exact(chunk):
+    """Integer inputs with negative weights only: scores <= 0, many exact
+    ties (zero scores and repeated values), one chunk or several."""
+    S, T, H, D, m, k = 2048, 3000, 8, 32, 1, 700
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=80, dtype=torch.bfloat16)
+    w = -w
+    say("negative integer weights chunk=%d" % chunk)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, chunk_keys=chunk)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
 # -------------------------------------------------------------- medium ----
 
 def test_medium_bf16_gaussian_full():

@@ -341,19 +341,30 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         pend = false;
     };
 
-    auto compute_tile = [&](const unsigned char *tb, int t) {
+    // B fragments of two half-steps; with double-buffered tiles bb[0] holds
+    // the next tile's first fragments when a tile starts (read early, see
+    // the tile loop below).
+    bf16x8 bb[2][HALF];
+    // retire(): the barrier of a double-buffered tile and what follows it,
+    // called by every wave once per tile; a wave with work in the tile calls
+    // it before the tile's last step (whose B fragments are in registers by
+    // then), so that the next tile's first LDS reads overlap that step's
+    // MFMAs instead of stalling every wave after the barrier.
+    auto compute_tile = [&](const unsigned char *tb, int t, auto &&retire) {
         const int rel_t = t * NT;  // tile start relative to the chunk
         if (active && rel_t < my_len) {
-            bf16x8 bb[2][HALF];
             float pacc = 0.0f;  // share of the block being finished
             float pe = 0.0f;    // share of the even block of the current pair
             const bool real_c = pend;
-            load_b(tb, 0, 0, bb[0]);
+            if constexpr (!DB) load_b(tb, 0, 0, bb[0]);
 #pragma unroll
             for (int step = 0; step < 2 * NB; ++step) {
                 const int kb = step >> 1, hs = step & 1;
                 if (step + 1 < 2 * NB)
                     load_b(tb, (step + 1) >> 1, (step + 1) & 1, bb[(step + 1) & 1]);
+                if constexpr (DB) {
+                    if (step == 2 * NB - 1) retire();
+                }
                 // Keep the prefetch here, one step ahead of its use.
                 __builtin_amdgcn_sched_barrier(0);
                 mfma_half(bb[step & 1], hs, acc[kb & 1]);
@@ -370,26 +381,36 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
             pe_c = pe;  // the tile's last pair (blocks NB-2, NB-1) is carried
             rel_c = rel_t + (NB - 2) * 32;
             pend = true;
-        } else if (pend) {
-            flush();
+        } else {
+            if (pend) flush();
+            if constexpr (DB) retire();
         }
     };
+    auto no_retire = []() {};
 
     if constexpr (DB) {
-        // Tile t+1 is DMA'd into the other buffer while tile t is computed;
-        // the barrier after each tile (whose fence waits for the DMA) makes
-        // the new tile visible and frees the old one.  Unrolled by two so
-        // that every access names its buffer at compile time.
+        // Tile t+1 is DMA'd into the other buffer while tile t is computed.
+        // The barrier that retires tile t (its fence waits for the DMA of
+        // tile t+1) makes tile t+1 visible and frees tile t's buffer for
+        // the DMA of tile t+2, which is issued right after it together with
+        // the first B-fragment reads of tile t+1.  Unrolled by two so that
+        // every access names its buffer at compile time.
         dma(tile_a, 0);
         __syncthreads();
+        if (ntiles > 1) dma(tile_b, 1);
+        if (active && my_len > 0) load_b(tile_a, 0, 0, bb[0]);
         for (int t = 0; t < ntiles; t += 2) {
-            if (t + 1 < ntiles) dma(tile_b, t + 1);
-            compute_tile(tile_a, t);
-            __syncthreads();
+            compute_tile(tile_a, t, [&]() {
+                __syncthreads();
+                if (t + 2 < ntiles) dma(tile_a, t + 2);
+                if (t + 1 < ntiles && active && (t + 1) * NT < my_len) load_b(tile_b, 0, 0, bb[0]);
+            });
             if (t + 1 >= ntiles) break;
-            if (t + 2 < ntiles) dma(tile_a, t + 2);
-            compute_tile(tile_b, t + 1);
-            __syncthreads();
+            compute_tile(tile_b, t + 1, [&]() {
+                __syncthreads();
+                if (t + 3 < ntiles) dma(tile_b, t + 3);
+                if (t + 2 < ntiles && active && (t + 2) * NT < my_len) load_b(tile_a, 0, 0, bb[0]);
+            });
         }
     } else {
         gload(0);
@@ -398,7 +419,7 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         for (int t = 0; t < ntiles; ++t) {
             const bool more = t + 1 < ntiles;
             if (more) gload(t + 1);
-            compute_tile(lds, t);
+            compute_tile(lds, t, no_retire);
             if (more) {
                 __syncthreads();  // single buffer: all reads done
                 lstore(0);

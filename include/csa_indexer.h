@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 /* Status codes. */
 #define CSA_OK 0
@@ -179,9 +179,48 @@ int csa_indexer_topk_batched(const void *q, const void *w, const void *kc, int32
 #define CSA_KERNEL_SCORE 0  /* chunk scoring: MFMA contraction + ReLU + head sum */
 #define CSA_KERNEL_SELECT 1 /* chunk top-k, merge into running lists, emit */
 #define CSA_KERNEL_MERGE 2  /* merge rounds of key-split lists, emit */
-#define CSA_KERNEL_KINDS 3
+#define CSA_KERNEL_ATTENTION 3 /* sparse attention over the selected entries */
+#define CSA_KERNEL_KINDS 4
 int csa_profile_enable(int enable);
 int csa_profile_collect(double *ms_out, int64_t *launches_out, int32_t n_kinds);
+
+/*
+ * Sparse attention over each query's selected entries: the consumer of the
+ * indexer's output in the CSA pipeline.  The page ("StreamIndex: Memory-
+ * Bounded Compressed Sparse Attention via Streaming Top-k", Abstract) says
+ * that a sparse attention kernel reads only the selected compressed entries
+ * and gives no formula or dimensions for it.  This function computes the
+ * plain softmax attention of each query row over its selected entries in
+ * the shared-latent (multi-query) form: all H heads attend over the same
+ * entries; an entry's latent row kv[e, :] is the key and its first D_V
+ * dims are the value:
+ *
+ *   out[i,h,:] = sum_{e in sel(i)} p_{h,e} kv[e, :D_V],
+ *   p_{h,e}    = softmax over e of (scale * q[i,h,:] . kv[e,:])
+ *
+ * where sel(i) lists idx[i, :] without its -1 entries (an entry listed twice
+ * counts twice).  A row with nothing selected gives zeros.
+ *
+ *   q    [S][H][D_K]   bf16   (16-byte aligned)
+ *   kv   [T][D_K]      bf16   (16-byte aligned; may be NULL when T == 0)
+ *   idx  [S][k]        int32  (4-byte aligned; may be NULL when k == 0)
+ *   out  [S][H][D_V]   bf16   (2-byte aligned), fully overwritten
+ *
+ * idx entries must be -1 or in [0, T): this is what csa_indexer_topk
+ * writes.  Other values are not detected; they read zeros (memory-safe).
+ * Logits and the softmax are fp32 (exp2 based, reference max moved lazily),
+ * the weights are rounded to bf16 for the weighted sum, which accumulates in
+ * fp32; out is rounded to bf16.
+ *
+ * dtype must be CSA_BF16 (CSA_F32 gives CSA_ERR_UNSUPPORTED).  This build
+ * supports H in {32, 64} and (D_K, D_V) in {(576, 512), (128, 128)}; other
+ * positive shapes give CSA_ERR_UNSUPPORTED, as do k > 2^20, S > 2^31 - 1 and
+ * T * D_K * 2 >= 2^31.  scale must be finite (else CSA_ERR_BAD_SHAPE).
+ * Enqueued on `stream`; allocates nothing; needs no workspace.
+ */
+int csa_sparse_attention(const void *q, const void *kv, const int32_t *idx, void *out,
+                         int32_t dtype, int64_t S, int64_t T, int32_t H, int32_t D_K,
+                         int32_t D_V, int64_t k, float scale, void *stream);
 
 #ifdef __cplusplus
 }

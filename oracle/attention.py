@@ -39,6 +39,29 @@ def sparse_attention_row(q_row, kv, sel, d_v, scale):
     return p @ lat[:, :d_v]
 
 
+def sparse_attention_with_magnitude(q, kv, idx, d_v, scale, rows=None):
+    """As sparse_attention, plus mag[r, h, :] = sum_e p_{h,e} |kv[e, :d_v]|,
+    the size of the terms each output element sums (what rounding errors of
+    the weights scale with)."""
+    q = np.asarray(q)
+    idx = np.asarray(idx)
+    rows = range(q.shape[0]) if rows is None else rows
+    out = np.zeros((len(rows), q.shape[1], d_v), dtype=np.float64)
+    mag = np.zeros_like(out)
+    for r, i in enumerate(rows):
+        sel = idx[i][idx[i] >= 0]
+        if len(sel) == 0:
+            continue
+        lat = np.asarray(kv, dtype=np.float64)[sel.astype(np.int64)]
+        logits = scale * (np.asarray(q[i], dtype=np.float64) @ lat.T)
+        logits = logits - logits.max(axis=1, keepdims=True)
+        p = np.exp(logits)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[r] = p @ lat[:, :d_v]
+        mag[r] = p @ np.abs(lat[:, :d_v])
+    return out, mag
+
+
 def sparse_attention(q, kv, idx, d_v, scale, rows=None):
     """q [S, H, D_K], kv [T, D_K], idx [S, k] (int, -1 = none): out
     [len(rows), H, d_v] float64 for the given rows (default: all)."""

@@ -21,12 +21,13 @@ CSA_BF16 = 1
 CSA_KERNEL_SCORE = 0
 CSA_KERNEL_SELECT = 1
 CSA_KERNEL_MERGE = 2
-CSA_KERNEL_KINDS = 3
-KERNEL_NAMES = ("score", "select", "merge")
+CSA_KERNEL_ATTENTION = 3
+CSA_KERNEL_KINDS = 4
+KERNEL_NAMES = ("score", "select", "merge", "attention")
 
 EXPORTS = ("csa_abi_version", "csa_status_str", "csa_indexer_topk_workspace_size",
            "csa_indexer_topk", "csa_indexer_topk_batched", "csa_profile_enable",
-           "csa_profile_collect")
+           "csa_profile_collect", "csa_sparse_attention")
 
 
 class CsaError(RuntimeError):
@@ -82,6 +83,9 @@ def load_library(path: str | None = None):
     lib.csa_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_int64), i32]
     lib.csa_profile_collect.restype = ctypes.c_int
+    lib.csa_sparse_attention.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i64,
+                                         ctypes.c_float, vp]
+    lib.csa_sparse_attention.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -202,6 +206,49 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
                 ctypes.c_void_p(workspace.data_ptr()), nbytes, ctypes.byref(o),
                 ctypes.c_void_p(stream)))
     return idx, score
+
+
+def sparse_attention(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, d_v: int, *,
+                     scale: float | None = None, out: torch.Tensor | None = None):
+    """Sparse attention of each query row over its selected entries (the CSA
+    consumer of ``topk``'s idx), shared-latent form: all heads attend over
+    the same entries, kv[e, :] is an entry's key and kv[e, :d_v] its value.
+
+    q [S, H, D_K], kv [T, D_K] bfloat16, idx [S, k] int32 (-1 = none), all
+    contiguous on one GPU.  scale defaults to 1/sqrt(D_K).  Returns out
+    [S, H, d_v] bfloat16.  Runs on torch's current stream.
+    """
+    if q.dim() != 3 or kv.dim() != 2 or idx.dim() != 2:
+        raise ValueError("q must be [S,H,D_K], kv [T,D_K], idx [S,k]")
+    S, H, DK = q.shape
+    T = kv.shape[0]
+    if kv.shape[1] != DK or idx.shape[0] != S:
+        raise ValueError("shape mismatch: q %s, kv %s, idx %s"
+                         % (tuple(q.shape), tuple(kv.shape), tuple(idx.shape)))
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or idx.dtype != torch.int32:
+        raise TypeError("q and kv must be bfloat16, idx int32")
+    dev = q.device
+    if dev.type != "cuda" or kv.device != dev or idx.device != dev:
+        raise ValueError("q, kv, idx must be on one GPU device")
+    for name, t in (("q", q), ("kv", kv), ("idx", idx)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    k = idx.shape[1]
+    if scale is None:
+        scale = 1.0 / float(DK) ** 0.5
+    oshape = (S, H, int(d_v))
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.bfloat16, device=dev)
+    elif tuple(out.shape) != oshape or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor of shape %s" % (oshape,))
+    lib = load_library()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        _check(lib.csa_sparse_attention(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv.data_ptr()),
+            ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(out.data_ptr()), CSA_BF16,
+            S, T, H, DK, int(d_v), k, float(scale), ctypes.c_void_p(stream)))
+    return out
 
 
 def profile_enable(on: bool = True):

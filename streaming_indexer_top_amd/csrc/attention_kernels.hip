@@ -1,0 +1,307 @@
+// Sparse attention over the entries the lightning indexer selected, for gfx950.
+//
+// The page "StreamIndex: Memory-Bounded Compressed Sparse Attention via
+// Streaming Top-k" (Abstract) ends the CSA pipeline with a sparse attention
+// kernel that reads only the selected compressed entries.  It gives no
+// formula or dimensions for it; this kernel computes the plain softmax
+// attention of each query row over its selected entries in the shared-latent
+// (multi-query) form: all H heads attend over the same entries, an entry's
+// latent row is the key (dk dims) and its first dv dims are the value:
+//
+//   out[i,h,:] = sum_{e in sel(i)} p_{h,e} kv[e,:dv],
+//   p_{h,e} = softmax over e of (scale * q[i,h,:] . kv[e,:])
+//
+// sel(i) = idx[i,:] without its -1 padding; an empty selection gives zeros.
+//
+// One workgroup per query row, 4 waves per 32-head block.  Wave (hb, qq)
+// keeps its heads' q for k-steps qq*KQ .. qq*KQ+KQ-1 resident (a quarter of
+// dk), so every wave of a head block computes a partial 32x32 logit block per
+// 32-entry tile with v_mfma_f32_32x32x16_bf16; the four partials meet in LDS.
+// The selected latent rows are gathered into registers (each lane fetches
+// the 16 bytes its slot of the swizzled tile needs, straight from the row
+// the index names; -1 reads zeros through the buffer range check) almost a
+// tile ahead, and written to the free one of two static LDS tile buffers
+// just before the barrier that publishes them.  (An LDS DMA gather would
+// need no registers, but every barrier waits for all DMAs in flight, which
+// would leave it half a tile.)  Per tile:
+//   1. partial logits (MFMA, B fragments from the tile),
+//   2. barrier; wave qq of a head block finishes 8 of its 32 heads: sums the
+//      partials in a fixed order, masks padding, takes the tile max and runs
+//      an online softmax in base 2 whose reference max moves only when a
+//      head's max rises by more than 2^8 (the factor then rescales the
+//      accumulators; otherwise they are left alone), writes P (bf16) to LDS,
+//   3. barrier; P * V with v_mfma_f32_32x32x16_bf16, wave qq owning a quarter
+//      of the dv output dims: the V fragments (8 consecutive entries of one
+//      dim per lane) come from the row-major tile by ds_read_b64_tr_b16, two
+//      transposing 8-byte reads per fragment.
+// The softmax denominators are kept per lane and reduced once at the end.
+#include "csa_internal.h"
+
+namespace csa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 32;      // selected entries per tile
+constexpr float kTau = 8.0f;   // a head's reference max moves when its max rises by more than this (log2 units)
+constexpr int kPRow = 40;      // P row stride in bf16 elements (32 entries + padding against bank conflicts)
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// Transposing LDS read: within each 16-lane group, lane o receives element
+// o%4 of the 8-byte rows that lanes o/4, o/4+4, o/4+8, o/4+12 point at.
+__device__ inline i16x4 read_tr16(const unsigned char *p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (i16x4 __attribute__((address_space(3))) *)(p));
+}
+
+template <int DK, int DV, int HB>
+__global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
+{
+    constexpr int WAVES = 4 * HB;
+    constexpr int KQ = DK / 64;         // 16-dim k-steps per quarter of dk
+    constexpr int NBW = DV / 128;       // 32-dim output blocks per wave
+    constexpr int ROWB = DK * 2;        // bytes per latent row
+    constexpr int TILEB = kTile * ROWB; // bytes per tile
+    constexpr int NPIECE = TILEB / 1024;
+    constexpr int PPW = (NPIECE + WAVES - 1) / WAVES;  // DMA pieces per wave
+    static_assert(DK % 64 == 0 && DV % 128 == 0 && DV <= DK, "shape");
+    static_assert(TILEB % 1024 == 0 && (DK / 8) % 8 == 0, "whole DMA pieces, 8-chunk swizzle");
+
+    __shared__ __attribute__((aligned(16))) unsigned char tile0[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char tile1[TILEB];
+    __shared__ __attribute__((aligned(16))) f32x4 part[WAVES][4][64];  // [wave][row quad][lane]
+    __shared__ __attribute__((aligned(16))) __bf16 pbuf[HB * 32][kPRow];
+    __shared__ __attribute__((aligned(16))) float alpha_s[HB * 32];
+    __shared__ __attribute__((aligned(16))) float l_s[HB * 32];
+    __shared__ int flag_s[WAVES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hb = wave >> 2, qq = wave & 3;
+    const int col = lane & 31, half = lane >> 5;
+    const int64_t row = blockIdx.x;
+    const int k = a.k;
+    const int ntiles = (k + kTile - 1) / kTile;
+    const int32_t *irow = a.idx + row * (int64_t)k;
+
+    // Resident q: head hb*32+col, dims (qq*KQ + j)*16 + half*8 .. +7.
+    bf16x8 qf[KQ];
+    {
+        const __bf16 *qh = (const __bf16 *)a.q + ((int64_t)row * a.H + hb * 32 + col) * DK;
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) qf[j] = *(const bf16x8 *)(qh + (qq * KQ + j) * 16 + half * 8);
+    }
+
+    // Entry index of tile row (lane % 32) of tile t, -1 past k.
+    auto load_idx = [&](int t) -> int {
+        const int e = t * kTile + col;
+        return (t < ntiles && e < k) ? irow[e] : -1;
+    };
+    // Gather of one tile: piece p of the tile is 1 KiB; its lane l holds
+    // bytes [16l, 16l+16) of the piece, i.e. row r, slot s of the tile,
+    // which is chunk s ^ (r % 8) of latent row idx[r] (the swizzle spreads a
+    // B-fragment read over the banks).
+    const __amdgpu_buffer_rsrc_t kv_rs = buffer_rsrc(a.kv, (uint32_t)(a.T * ROWB));
+    u32x4 st[PPW];
+    auto gload = [&](int iv) {
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+            const int p = j * WAVES + wave;
+            const int pos = p * 1024 + lane * 16;
+            const int r = (pos / ROWB) & 31;  // pieces past the tile (p >= NPIECE) are never stored
+            const int chunk = ((pos % ROWB) >> 4) ^ (r & 7);
+            const int e = __shfl(iv, r);
+            const int off = e >= 0 ? e * ROWB + chunk * 16 : (int)0x80000000;
+            st[j] = __builtin_amdgcn_raw_buffer_load_b128(kv_rs, off, 0, 0);
+        }
+    };
+    auto lstore = [&](unsigned char *dst) {
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) {
+            const int p = j * WAVES + wave;
+            if (p < NPIECE) *(u32x4 *)(dst + p * 1024 + lane * 16) = st[j];  // wave-uniform test
+        }
+    };
+
+    f32x16 o[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) o[nb] = f32x16{};
+    float mref[4], lsum[4];  // reference max and per-lane denominators of heads 8qq+4half+ii
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        mref[ii] = -__builtin_inff();
+        lsum[ii] = 0.0f;
+    }
+    const float c2 = a.scale_log2e;
+    int ivn = -1;  // entry indices of the next tile to gather
+
+    // Tile t in buffer tb (published by the previous tile's second barrier);
+    // next: the other buffer, which receives tile t+1 from the staging
+    // registers; vmask: which rows of tile t hold an entry.  Returns the
+    // row mask of tile t+2, whose gather it starts.
+    auto step = [&](const unsigned char *tb, unsigned char *next, uint32_t vmask, int t) -> uint32_t {
+        // 1. partial logits of head block hb over this wave's quarter of dk.
+        f32x16 acc = {};
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+            const int c = 2 * (qq * KQ + j) + half;
+            const bf16x8 b = *(const bf16x8 *)(tb + col * ROWB + ((c ^ (col & 7)) << 4));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], b, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+            part[wave][r4][lane] = f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+        __syncthreads();
+        // 2. heads 8qq + 4half + ii (accumulator rows 4qq + ii), entry col.
+        f32x4 s = part[hb * 4][qq][lane];
+#pragma unroll
+        for (int w2 = 1; w2 < 4; ++w2) s += part[hb * 4 + w2][qq][lane];
+        const bool valid = (vmask >> col) & 1u;
+        bool need_any = false;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const float x = valid ? s[ii] * c2 : -__builtin_inff();
+            float mx = x;
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            float alpha = 1.0f;
+            const bool need = mx > mref[ii] + kTau;
+            if (need) {
+                alpha = __builtin_amdgcn_exp2f(mref[ii] - mx);
+                mref[ii] = mx;
+            }
+            need_any |= need;
+            const float p = mref[ii] == -__builtin_inff() ? 0.0f
+                                                          : __builtin_amdgcn_exp2f(x - mref[ii]);
+            lsum[ii] = lsum[ii] * alpha + p;
+            const int hrow = 8 * qq + 4 * half + ii;
+            pbuf[hb * 32 + hrow][col] = (__bf16)p;
+            if (col == 0) alpha_s[hb * 32 + hrow] = alpha;
+        }
+        const bool wave_need = __ballot(need_any) != 0;
+        if (lane == 0) flag_s[wave] = wave_need ? 1 : 0;
+        // Tile t+1 into the other buffer (its last reader, P V of tile t-1,
+        // finished before the first barrier of this tile), then the gather
+        // of tile t+2 into the freed registers.
+        if (t + 1 < ntiles) lstore(next);
+        uint32_t vm2 = 0;
+        if (t + 2 < ntiles) {
+            vm2 = (uint32_t)__ballot(ivn >= 0);
+            gload(ivn);
+            ivn = load_idx(t + 3);
+        }
+        __syncthreads();
+        // 3. O = alpha * O + P V for head block hb, dims qq*DV/4 .. +DV/4-1.
+        const bool resc = (flag_s[hb * 4] | flag_s[hb * 4 + 1] | flag_s[hb * 4 + 2] |
+                           flag_s[hb * 4 + 3]) != 0;  // block-uniform
+        if (resc) {
+#pragma unroll
+            for (int j4 = 0; j4 < 4; ++j4) {
+                const f32x4 al = *(const f32x4 *)&alpha_s[hb * 32 + 8 * j4 + 4 * half];
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) o[nb][4 * j4 + ii] *= al[ii];
+            }
+        }
+        const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 pa = *(const bf16x8 *)&pbuf[hb * 32 + col][kk * 16 + half * 8];
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const int dim = qq * (DV / 4) + nb * 32 + 16 * (g & 1) + 4 * (sl & 3);
+                const int e0 = kk * 16 + (g >> 1) * 8 + (sl >> 2);
+                const int e1 = e0 + 4;
+                const i16x4 v0 = read_tr16(tb + e0 * ROWB + ((((dim >> 3) ^ (e0 & 7))) << 4) + (dim & 7) * 2);
+                const i16x4 v1 = read_tr16(tb + e1 * ROWB + ((((dim >> 3) ^ (e1 & 7))) << 4) + (dim & 7) * 2);
+                const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, __builtin_bit_cast(bf16x8, vv),
+                                                                o[nb], 0, 0, 0);
+            }
+        }
+        return vm2;
+    };
+
+    // Tiles alternate between the two buffers (the loop is unrolled by two
+    // so that every access names its buffer), and so do the row masks.
+    uint32_t vmE = 0, vmO = 0;
+    if (ntiles > 0) {
+        const int iv0 = load_idx(0), iv1 = load_idx(1);
+        vmE = (uint32_t)__ballot(iv0 >= 0);
+        vmO = (uint32_t)__ballot(iv1 >= 0);
+        gload(iv0);
+        lstore(tile0);
+        if (ntiles > 1) gload(iv1);
+        ivn = load_idx(2);
+    }
+    __syncthreads();
+    for (int t = 0; t < ntiles; t += 2) {
+        vmE = step(tile0, tile1, vmE, t);
+        if (t + 1 >= ntiles) break;
+        vmO = step(tile1, tile0, vmO, t + 1);
+    }
+
+    // Denominators: sum the per-lane shares of each head over its 32 lanes.
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        float l = lsum[ii];
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) l += __shfl_xor(l, off);
+        if (col == 0) l_s[hb * 32 + 8 * qq + 4 * half + ii] = l;
+    }
+    __syncthreads();
+    __bf16 *orow = (__bf16 *)a.out + (int64_t)row * a.H * DV;
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4) {
+        const f32x4 l4 = *(const f32x4 *)&l_s[hb * 32 + 8 * j4 + 4 * half];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int head = hb * 32 + 8 * j4 + 4 * half + ii;
+            const float inv = l4[ii] > 0.0f ? 1.0f / l4[ii] : 0.0f;
+#pragma unroll
+            for (int nb = 0; nb < NBW; ++nb) {
+                const int dim = qq * (DV / 4) + nb * 32 + col;
+                orow[(int64_t)head * DV + dim] = (__bf16)(o[nb][4 * j4 + ii] * inv);
+            }
+        }
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const AttnArgs &a, hipStream_t s)
+{
+    if (a.H == 32) attention_kernel<DK, DV, 1><<<dim3((unsigned)a.S), 256, 0, s>>>(a);
+    else if (a.H == 64) attention_kernel<DK, DV, 2><<<dim3((unsigned)a.S), 512, 0, s>>>(a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool attention_shape_supported(int32_t H, int32_t dk, int32_t dv)
+{
+    return (H == 32 || H == 64) && ((dk == 576 && dv == 512) || (dk == 128 && dv == 128));
+}
+
+hipError_t launch_attention(const AttnArgs &a, int32_t dk, int32_t dv, hipStream_t stream)
+{
+    if (a.S <= 0) return hipSuccess;
+    if (dk == 576 && dv == 512) return launch_dims<576, 512>(a, stream);
+    if (dk == 128 && dv == 128) return launch_dims<128, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace csa

@@ -16,10 +16,12 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <cmath>
 #include <mutex>
 #include <vector>
 
 #include "../../include/csa_indexer.h"
+
 #include "csa_internal.h"
 
 namespace {
@@ -447,6 +449,36 @@ int csa_indexer_topk_batched(const void *q, const void *w, const void *kc, int32
         if (sb != CSA_OK) return sb;
     }
     return CSA_OK;
+}
+
+int csa_sparse_attention(const void *q, const void *kv, const int32_t *idx, void *out,
+                         int32_t dtype, int64_t S, int64_t T, int32_t H, int32_t D_K,
+                         int32_t D_V, int64_t k, float scale, void *stream)
+{
+    if (S < 0 || T < 0 || k < 0 || H <= 0 || D_K <= 0 || D_V <= 0) return CSA_ERR_BAD_SHAPE;
+    if (dtype != CSA_BF16) return dtype == CSA_F32 ? CSA_ERR_UNSUPPORTED : CSA_ERR_BAD_DTYPE;
+    if (!std::isfinite(scale)) return CSA_ERR_BAD_SHAPE;
+    if (!csa::attention_shape_supported(H, D_K, D_V)) return CSA_ERR_UNSUPPORTED;
+    if (k > ((int64_t)1 << 20) || S > INT32_MAX || T * D_K * 2 >= ((int64_t)1 << 31))
+        return CSA_ERR_UNSUPPORTED;
+    if (S == 0) return CSA_OK;
+    if (!q || !out || (k > 0 && !idx) || (T > 0 && !kv)) return CSA_ERR_NULL_PTR;
+    if (((uintptr_t)q & 15) || ((uintptr_t)kv & 15) || ((uintptr_t)idx & 3) ||
+        ((uintptr_t)out & 1))
+        return CSA_ERR_MISALIGNED;
+    csa::AttnArgs a;
+    a.q = q;
+    a.kv = kv;
+    a.idx = idx;
+    a.out = out;
+    a.S = S;
+    a.T = T;
+    a.H = H;
+    a.k = (int32_t)k;
+    a.scale_log2e = scale * 1.4426950408889634f;
+    hipStream_t s = (hipStream_t)stream;
+    return launch_timed(CSA_KERNEL_ATTENTION, s,
+                        [&] { return csa::launch_attention(a, D_K, D_V, s); });
 }
 
 int csa_profile_enable(int enable)

@@ -123,6 +123,24 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 // Merge kernel: one workgroup per (row, list pair) of a merge round.
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
+// Sparse attention over each query row's selected entries (one workgroup
+// per row): q [S][H][dk] bf16, kv [T][dk] bf16 (the value of an entry is
+// the first dv dims of its row), idx [S][k] int32 (-1 = none), out
+// [S][H][dv] bf16.
+struct AttnArgs {
+    const void *q;
+    const void *kv;
+    const int32_t *idx;
+    void *out;
+    int64_t S, T;
+    int32_t H, k;
+    float scale_log2e;  // softmax scale times log2(e): the kernel uses exp2
+};
+
+// Supported shapes: H in {32, 64}; (dk, dv) in {(576, 512), (128, 128)}.
+bool attention_shape_supported(int32_t H, int32_t dk, int32_t dv);
+hipError_t launch_attention(const AttnArgs &a, int32_t dk, int32_t dv, hipStream_t stream);
+
 // Keys of one chunk piece that the select kernel stages in LDS at a time.
 constexpr int kSelectPiece = 2048;
 constexpr int kSelectThreads = 256;

@@ -97,6 +97,15 @@ def bf16_mixture(S: int, T: int, H: int, D: int, seed: int, device="cpu",
     return q, w, kc
 
 
+def attention_gaussian(S: int, T: int, H: int, DK: int, seed: int, device="cpu"):
+    """Inputs of the sparse attention: q [S, H, DK] and the latent rows kv
+    [T, DK], entries N(0, 1) drawn in fp32 and rounded to bf16."""
+    g = _gen(seed, device)
+    q = _randn_sliced((S, H, DK), g, device, 1.0, torch.bfloat16)
+    kv = _randn_sliced((T, DK), g, device, 1.0, torch.bfloat16)
+    return q, kv
+
+
 def sample_rows(S: int, m: int, k: int, count: int, seed: int):
     """A fixed set of query rows to check at sizes where the oracle cannot
     take every row: the boundary rows (first rows, the first row with a key,

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = csa.load_library()
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
     for st in range(0, 10):
         assert lib.csa_status_str(st)
 
@@ -169,3 +169,41 @@ def test_python_binding_rejects_bad_tensors():
         csa.topk(q, w.float(), kc, 4, 2)
     with pytest.raises(ValueError):
         csa.topk(q, w[:3], kc, 4, 2)
+
+
+@pytest.mark.parametrize("args, status", [
+    # (S, T, H, D_K, D_V, k, dtype, scale)
+    ((-1, 10, 64, 576, 512, 8, binding.CSA_BF16, 0.1), 2),
+    ((4, 10, 64, 576, 512, -1, binding.CSA_BF16, 0.1), 2),
+    ((4, 10, 0, 576, 512, 8, binding.CSA_BF16, 0.1), 2),
+    ((4, 10, 64, 576, 512, 8, binding.CSA_BF16, float("nan")), 2),
+    ((4, 10, 64, 576, 512, 8, binding.CSA_BF16, float("inf")), 2),
+    ((4, 10, 64, 576, 512, 8, 7, 0.1), 3),
+    ((4, 10, 64, 576, 512, 8, binding.CSA_F32, 0.1), 6),
+    ((4, 10, 48, 576, 512, 8, binding.CSA_BF16, 0.1), 6),
+    ((4, 10, 64, 256, 256, 8, binding.CSA_BF16, 0.1), 6),
+    ((4, 10, 64, 576, 512, (1 << 20) + 1, binding.CSA_BF16, 0.1), 6),
+    ((4, 1 << 21, 64, 576, 512, 8, binding.CSA_BF16, 0.1), 6),
+])
+def test_sparse_attention_argument_checks(args, status):
+    """Bad shapes, dtypes, scales and unsupported sizes are refused before
+    any HIP call (dummy pointers: nothing is dereferenced)."""
+    S, T, H, DK, DV, k, dt, scale = args
+    lib = csa.load_library()
+    p = ctypes.c_void_p(256)
+    assert lib.csa_sparse_attention(p, p, p, p, dt, S, T, H, DK, DV, k, scale, None) == status
+
+
+def test_sparse_attention_null_and_alignment_checks():
+    lib = csa.load_library()
+    p, z = ctypes.c_void_p(256), ctypes.c_void_p(0)
+    a = (binding.CSA_BF16, 4, 10, 64, 576, 512, 8, 0.1, None)
+    assert lib.csa_sparse_attention(z, p, p, p, *a) == 1
+    assert lib.csa_sparse_attention(p, z, p, p, *a) == 1
+    assert lib.csa_sparse_attention(p, p, z, p, *a) == 1
+    assert lib.csa_sparse_attention(p, p, p, z, *a) == 1
+    assert lib.csa_sparse_attention(ctypes.c_void_p(264), p, p, p, *a) == 4
+    assert lib.csa_sparse_attention(p, p, ctypes.c_void_p(258), p, *a) == 4
+    # No rows: nothing to do, nothing touched.
+    assert lib.csa_sparse_attention(z, z, z, z, binding.CSA_BF16, 0, 10, 64, 576, 512, 8,
+                                    0.1, None) == 0

@@ -186,3 +186,19 @@ def test_pins_pass_on_the_oracle():
 @pytest.mark.parametrize("mutant", _mutants(), ids=lambda f: f.__name__)
 def test_pins_catch_planted_mistake(mutant):
     assert not _pins_pass(mutant)
+
+
+def test_magnitude_variant_agrees_and_bounds():
+    """The magnitude companion returns the same outputs, a sum of |values|
+    that bounds them, and equals them when every value is nonnegative."""
+    rng = np.random.default_rng(5)
+    kv = rng.standard_normal((60, 20))
+    q = rng.standard_normal((5, 4, 20))
+    idx = rng.integers(-1, 60, (5, 13))
+    out = att.sparse_attention(q, kv, idx, 12, 0.4)
+    out2, mag = att.sparse_attention_with_magnitude(q, kv, idx, 12, 0.4)
+    assert np.allclose(out, out2, rtol=1e-14, atol=1e-14)
+    assert np.all(mag >= np.abs(out) - 1e-14)
+    kvp = np.abs(kv)
+    o3, m3 = att.sparse_attention_with_magnitude(q, kvp, idx, 12, 0.4)
+    assert np.allclose(o3, m3, rtol=1e-14, atol=1e-14)

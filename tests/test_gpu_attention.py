@@ -1,0 +1,132 @@
+"""GPU parity of the sparse attention (``csa_sparse_attention`` through the C
+ABI) against the float64 oracle in ``oracle/attention.py``.
+
+Tolerance, from the arithmetic: logits are fp32 sums of exact bf16 products;
+the softmax weights are fp32 and rounded to bf16 (relative error <= 2^-9
+each) for the weighted sum, which accumulates in fp32, while the normaliser
+sums the unrounded weights; the output is rounded to bf16 (<= 2^-9 of it).
+So every element obeys
+
+    |out - ref| <= 2^-8 * (|ref| + sum_e p_e |v_e|) + 1e-6
+
+with sum_e p_e |v_e| from the oracle, leaving room for the fp32 logit error.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import streaming_indexer_top_amd as csa
+from oracle import attention as att
+from streaming_indexer_top_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_and_check(q, kv, idx, d_v, scale, rows=None):
+    out = csa.sparse_attention(q.to(DEV), kv.to(DEV), idx.to(DEV), d_v, scale=scale)
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    rows = list(range(q.shape[0])) if rows is None else list(rows)
+    ref, mag = att.sparse_attention_with_magnitude(q.float().numpy(), kv.float().numpy(),
+                                                   idx.numpy(), d_v, scale, rows=rows)
+    g = g[rows]
+    err = np.abs(g - ref)
+    bound = 2.0 ** -8 * (np.abs(ref) + mag) + 1e-6
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, "first failures (row, head, dim): %s; err %s bound %s" % (
+        bad[:5].tolist(), err[tuple(bad[0])], bound[tuple(bad[0])])
+    return g, ref
+
+
+def random_selection(rng, S, T, k, pad_frac=0.2):
+    idx = rng.integers(0, T, (S, k)).astype(np.int32)
+    for i in range(S):
+        n = int(rng.integers(0, k + 1)) if rng.random() < pad_frac else k
+        idx[i, n:] = -1
+    return torch.from_numpy(idx)
+
+
+@pytest.mark.parametrize("H", [32, 64])
+@pytest.mark.parametrize("dims", [(576, 512), (128, 128)])
+@pytest.mark.parametrize("k", [1, 31, 32, 33, 100, 2048])
+def test_random_selections(H, dims, k):
+    DK, DV = dims
+    S, T = 37, 3000
+    say("attention H=%d dk=%d dv=%d k=%d" % (H, DK, DV, k))
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=100 + k + H + DK)
+    rng = np.random.default_rng(k * 7 + H)
+    idx = random_selection(rng, S, T, k)
+    idx[0, :] = -1                      # a row with nothing selected
+    if k >= 4:
+        idx[1, : k // 2] = idx[1, 0]    # a row with repeated entries
+    g, _ = run_and_check(q, kv, idx, DV, 1.0 / DK ** 0.5)
+    assert np.all(g[0] == 0.0)
+
+
+def test_no_entries_at_all():
+    S, T, H, DK, DV = 5, 10, 64, 576, 512
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=7)
+    idx = torch.empty((S, 0), dtype=torch.int32)
+    out = csa.sparse_attention(q.to(DEV), kv.to(DEV), idx.to(DEV), DV)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+def test_growing_logits_move_the_reference_max():
+    """Entries ordered by rising logit and a large scale: each tile's max
+    rises by far more than the lazy-rescale threshold, so the accumulators
+    are rescaled again and again; a single dominant entry at the end must
+    win."""
+    S, T, H, DK, DV, k = 8, 4096, 64, 576, 512, 512
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=9)
+    rng = np.random.default_rng(9)
+    idx = np.zeros((S, k), dtype=np.int32)
+    qf, kf = q.float().numpy(), kv.float().numpy()
+    for i in range(S):
+        sel = rng.choice(T, k, replace=False)
+        score = (qf[i, 0] @ kf[sel].T)          # head 0's logits
+        idx[i] = sel[np.argsort(score)]         # ascending: maxima keep rising
+    run_and_check(q, kv, torch.from_numpy(idx), DV, 0.5)
+
+
+def test_indexer_selection_feeds_attention():
+    """The composition the page runs: the indexer's top-k (causal padding
+    with -1 included) drives the attention; checked on every row."""
+    S, T, Hi, Di, m, k = 256, 64, 64, 128, 4, 40
+    qi, wi, kc = inputs.bf16_gaussian(S, T, Hi, Di, seed=12)
+    idx, _ = csa.topk(qi.to(DEV), wi.to(DEV), kc.to(DEV), m, k)
+    torch.cuda.synchronize()
+    q, kv = inputs.attention_gaussian(S, T, 64, 576, seed=13)
+    run_and_check(q, kv, idx.cpu(), 512, 1.0 / 576 ** 0.5)
+
+
+def test_bench_shape_sampled_rows():
+    """The measured shape (64 heads, 576/512, k = 2048) at S = 8192 against
+    a 65,536-entry latent table, 48 rows checked."""
+    S, T, H, DK, DV, k = 8192, 65536, 64, 576, 512, 2048
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=21)
+    rng = np.random.default_rng(21)
+    idx = torch.from_numpy(rng.integers(0, T, (S, k)).astype(np.int32))
+    rows = sorted(set([0, 1, S - 1] + rng.integers(0, S, 45).tolist()))
+    run_and_check(q, kv, idx, DV, 1.0 / DK ** 0.5, rows=rows)
+
+
+def test_repeat_runs_bit_identical():
+    S, T, H, DK, DV, k = 64, 2000, 64, 576, 512, 300
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=31)
+    idx = random_selection(np.random.default_rng(31), S, T, k).to(DEV)
+    q, kv = q.to(DEV), kv.to(DEV)
+    a = csa.sparse_attention(q, kv, idx, DV)
+    b = csa.sparse_attention(q, kv, idx, DV)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -65,6 +65,28 @@ __device__ inline i16x4 read_tr16(const unsigned char *p)
         (i16x4 __attribute__((address_space(3))) *)(p));
 }
 
+// Max over the 32 lanes of each half-wave, returned to every lane of that
+// half: DPP shifts within rows of 16 lanes, one row broadcast to the next
+// row, then the last lane of each half read back.
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_f32(float v)
+{
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ inline float half_max(float x)
+{
+    x = fmaxf(x, dpp_f32<0x111, 0xF>(x));  // row_shr:1
+    x = fmaxf(x, dpp_f32<0x112, 0xF>(x));  // row_shr:2
+    x = fmaxf(x, dpp_f32<0x114, 0xF>(x));  // row_shr:4
+    x = fmaxf(x, dpp_f32<0x118, 0xF>(x));  // row_shr:8
+    x = fmaxf(x, dpp_f32<0x142, 0xA>(x));  // row_bcast:15 into rows 1 and 3
+    const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 31));
+    const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    return (threadIdx.x & 32) ? hi : lo;
+}
+
 template <int DK, int DV, int HB>
 __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
 {
@@ -162,20 +184,25 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         }
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-            part[wave][r4][lane] = f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+            if (r4 != qq)  // this wave reduces its own quarter from registers
+                part[wave][r4][lane] = f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
         __syncthreads();
         // 2. heads 8qq + 4half + ii (accumulator rows 4qq + ii), entry col.
-        f32x4 s = part[hb * 4][qq][lane];
+        // Partials summed in wave order (a fixed order for every quarter).
+        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int w2 = 1; w2 < 4; ++w2) s += part[hb * 4 + w2][qq][lane];
+        for (int w2 = 0; w2 < 4; ++w2) {
+            f32x4 pw;
+            if (w2 == qq) pw = f32x4{acc[4 * qq], acc[4 * qq + 1], acc[4 * qq + 2], acc[4 * qq + 3]};
+            else pw = part[hb * 4 + w2][qq][lane];
+            s = w2 == 0 ? pw : s + pw;
+        }
         const bool valid = (vmask >> col) & 1u;
         bool need_any = false;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             const float x = valid ? s[ii] * c2 : -__builtin_inff();
-            float mx = x;
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float mx = half_max(x);
             float alpha = 1.0f;
             const bool need = mx > mref[ii] + kTau;
             if (need) {

@@ -169,6 +169,33 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     const float c2 = a.scale_log2e;
     int ivn = -1;  // entry indices of the next tile to gather
 
+    // Per-lane byte offsets inside a tile, fixed for the whole row.
+    // Logit B fragments: entry col, chunk 2*(qq*KQ + j) + half, swizzled.
+    int qk_off[KQ];
+#pragma unroll
+    for (int j = 0; j < KQ; ++j)
+        qk_off[j] = col * ROWB + (((2 * (qq * KQ + j) + half) ^ (col & 7)) << 4);
+    // Value fragments read by the transposing loads: this lane points at
+    // entry kk*16 + eb + 4*s2 (s2: first or second half of its 8 entries),
+    // dims dl..dl+3 of output block nb; inside a tile that is byte
+    //   kk*16*ROWB + hi(nb) + tr_off[s2][parity(nb)]
+    // where hi(nb) is the 128-byte group of the block's chunks and the
+    // parity picks which half of that group, which the swizzle (entry % 8)
+    // permutes per lane.
+    const int eb = ((lane >> 5) * 8) + ((lane & 15) >> 2);
+    const int dl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int cq = qq * (DV / 32);  // first output chunk of this wave
+    int tr_off[2][2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int e = eb + 4 * s2;
+#pragma unroll
+        for (int par = 0; par < 2; ++par) {
+            const int bp = ((cq >> 2) + par) & 1;  // bit 2 of the block's first chunk
+            tr_off[s2][par] = e * ROWB + (((bp * 4 + (dl >> 3)) ^ (e & 7)) << 4) + (dl & 7) * 2;
+        }
+    }
+
     // Tile t in buffer tb (published by the previous tile's second barrier);
     // next: the other buffer, which receives tile t+1 from the staging
     // registers; vmask: which rows of tile t hold an entry.  Returns the
@@ -178,8 +205,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         f32x16 acc = {};
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
-            const int c = 2 * (qq * KQ + j) + half;
-            const bf16x8 b = *(const bf16x8 *)(tb + col * ROWB + ((c ^ (col & 7)) << 4));
+            const bf16x8 b = *(const bf16x8 *)(tb + qk_off[j]);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], b, acc, 0, 0, 0);
         }
 #pragma unroll
@@ -198,26 +224,41 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
             s = w2 == 0 ? pw : s + pw;
         }
         const bool valid = (vmask >> col) & 1u;
-        bool need_any = false;
+        float x[4];
+        bool exceed = false;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const float x = valid ? s[ii] * c2 : -__builtin_inff();
-            const float mx = half_max(x);
-            float alpha = 1.0f;
-            const bool need = mx > mref[ii] + kTau;
-            if (need) {
-                alpha = __builtin_amdgcn_exp2f(mref[ii] - mx);
-                mref[ii] = mx;
-            }
-            need_any |= need;
-            const float p = mref[ii] == -__builtin_inff() ? 0.0f
-                                                          : __builtin_amdgcn_exp2f(x - mref[ii]);
-            lsum[ii] = lsum[ii] * alpha + p;
-            const int hrow = 8 * qq + 4 * half + ii;
-            pbuf[hb * 32 + hrow][col] = (__bf16)p;
-            if (col == 0) alpha_s[hb * 32 + hrow] = alpha;
+            x[ii] = valid ? s[ii] * c2 : -__builtin_inff();
+            exceed |= x[ii] > mref[ii] + kTau;
         }
-        const bool wave_need = __ballot(need_any) != 0;
+        // A head's reference max moves only when some logit of the tile
+        // exceeds it by more than kTau; usually none does, and the tile
+        // maxima are not needed at all.
+        const bool wave_need = __ballot(exceed) != 0;  // wave-uniform
+        if (wave_need) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const float mx = half_max(x[ii]);
+                float alpha = 1.0f;
+                if (mx > mref[ii] + kTau) {
+                    alpha = __builtin_amdgcn_exp2f(mref[ii] - mx);
+                    mref[ii] = mx;
+                    lsum[ii] *= alpha;
+                }
+                if (col == 0) alpha_s[hb * 32 + 8 * qq + 4 * half + ii] = alpha;
+            }
+        } else if (col == 0) {
+            // Another wave of the head block may rescale: these heads keep 1.
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) alpha_s[hb * 32 + 8 * qq + 4 * half + ii] = 1.0f;
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const float p = mref[ii] == -__builtin_inff() ? 0.0f
+                                                          : __builtin_amdgcn_exp2f(x[ii] - mref[ii]);
+            lsum[ii] += p;
+            pbuf[hb * 32 + 8 * qq + 4 * half + ii][col] = (__bf16)p;
+        }
         if (lane == 0) flag_s[wave] = wave_need ? 1 : 0;
         // Tile t+1 into the other buffer (its last reader, P V of tile t-1,
         // finished before the first barrier of this tile), then the gather
@@ -243,17 +284,15 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
                     for (int ii = 0; ii < 4; ++ii) o[nb][4 * j4 + ii] *= al[ii];
             }
         }
-        const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const bf16x8 pa = *(const bf16x8 *)&pbuf[hb * 32 + col][kk * 16 + half * 8];
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
-                const int dim = qq * (DV / 4) + nb * 32 + 16 * (g & 1) + 4 * (sl & 3);
-                const int e0 = kk * 16 + (g >> 1) * 8 + (sl >> 2);
-                const int e1 = e0 + 4;
-                const i16x4 v0 = read_tr16(tb + e0 * ROWB + ((((dim >> 3) ^ (e0 & 7))) << 4) + (dim & 7) * 2);
-                const i16x4 v1 = read_tr16(tb + e1 * ROWB + ((((dim >> 3) ^ (e1 & 7))) << 4) + (dim & 7) * 2);
+                const int hi = ((cq + nb * 4) & ~7) * 16;  // wave-uniform
+                const unsigned char *vb = tb + kk * 16 * ROWB + hi;
+                const i16x4 v0 = read_tr16(vb + tr_off[0][nb & 1]);
+                const i16x4 v1 = read_tr16(vb + tr_off[1][nb & 1]);
                 const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                 o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, __builtin_bit_cast(bf16x8, vv),
                                                                 o[nb], 0, 0, 0);

@@ -19,11 +19,11 @@
 // 32-entry tile with v_mfma_f32_32x32x16_bf16; the four partials meet in LDS.
 // The selected latent rows are gathered into registers (each lane fetches
 // the 16 bytes its slot of the swizzled tile needs, straight from the row
-// the index names; -1 reads zeros through the buffer range check) almost a
-// tile ahead, and written to the free one of two static LDS tile buffers
-// just before the barrier that publishes them.  (An LDS DMA gather would
-// need no registers, but every barrier waits for all DMAs in flight, which
-// would leave it half a tile.)  Per tile:
+// the index names; -1 reads zeros through the buffer range check) a tile
+// ahead and written into the free one of three static LDS tile buffers
+// under the next tile's MFMAs.  (An LDS DMA gather would need no registers,
+// but every barrier waits for all DMAs in flight, which would leave it half
+// a tile.)  Per tile:
 //   1. partial logits (MFMA, B fragments from the tile),
 //   2. barrier; wave qq of a head block finishes 8 of its 32 heads: sums the
 //      partials in a fixed order, masks padding, takes the tile max and runs
@@ -102,6 +102,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
 
     __shared__ __attribute__((aligned(16))) unsigned char tile0[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char tile1[TILEB];
+    __shared__ __attribute__((aligned(16))) unsigned char tile2[TILEB];
     __shared__ __attribute__((aligned(16))) f32x4 part[WAVES][4][64];  // [wave][row quad][lane]
     __shared__ __attribute__((aligned(16))) __bf16 pbuf[HB * 32][kPRow];
     __shared__ __attribute__((aligned(16))) float alpha_s[HB * 32];
@@ -196,11 +197,11 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         }
     }
 
-    // Tile t in buffer tb (published by the previous tile's second barrier);
-    // next: the other buffer, which receives tile t+1 from the staging
-    // registers; vmask: which rows of tile t hold an entry.  Returns the
-    // row mask of tile t+2, whose gather it starts.
-    auto step = [&](const unsigned char *tb, unsigned char *next, uint32_t vmask, int t) -> uint32_t {
+    // Tile t in buffer tb (published by the barriers of tile t-1); store:
+    // the buffer that receives tile t+2 from the staging registers; vmask:
+    // which rows of tile t hold an entry.  Returns the row mask of tile t+3,
+    // whose gather it starts.
+    auto step = [&](const unsigned char *tb, unsigned char *store, uint32_t vmask, int t) -> uint32_t {
         // 1. partial logits of head block hb over this wave's quarter of dk.
         f32x16 acc = {};
 #pragma unroll
@@ -260,17 +261,17 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
             pbuf[hb * 32 + 8 * qq + 4 * half + ii][col] = (__bf16)p;
         }
         if (lane == 0) flag_s[wave] = wave_need ? 1 : 0;
-        // Tile t+1 into the other buffer (its last reader, P V of tile t-1,
-        // finished before the first barrier of this tile), then the gather
-        // of tile t+2 into the freed registers.
-        if (t + 1 < ntiles) lstore(next);
-        uint32_t vm2 = 0;
-        if (t + 2 < ntiles) {
-            vm2 = (uint32_t)__ballot(ivn >= 0);
-            gload(ivn);
-            ivn = load_idx(t + 3);
-        }
         __syncthreads();
+        // Tile t+2 into the buffer of tile t-1 (its last readers finished
+        // before this tile's first barrier), then the gather of tile t+3
+        // into the freed registers; both run under the MFMAs below.
+        if (t + 2 < ntiles) lstore(store);
+        uint32_t vm3 = 0;
+        if (t + 3 < ntiles) {
+            vm3 = (uint32_t)__ballot(ivn >= 0);
+            gload(ivn);
+            ivn = load_idx(t + 4);
+        }
         // 3. O = alpha * O + P V for head block hb, dims qq*DV/4 .. +DV/4-1.
         const bool resc = (flag_s[hb * 4] | flag_s[hb * 4 + 1] | flag_s[hb * 4 + 2] |
                            flag_s[hb * 4 + 3]) != 0;  // block-uniform
@@ -298,26 +299,33 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
                                                                 o[nb], 0, 0, 0);
             }
         }
-        return vm2;
+        return vm3;
     };
 
-    // Tiles alternate between the two buffers (the loop is unrolled by two
+    // Tiles rotate through the three buffers (the loop is unrolled by three
     // so that every access names its buffer), and so do the row masks.
-    uint32_t vmE = 0, vmO = 0;
+    uint32_t vmA = 0, vmB = 0, vmC = 0;
     if (ntiles > 0) {
-        const int iv0 = load_idx(0), iv1 = load_idx(1);
-        vmE = (uint32_t)__ballot(iv0 >= 0);
-        vmO = (uint32_t)__ballot(iv1 >= 0);
+        const int iv0 = load_idx(0), iv1 = load_idx(1), iv2 = load_idx(2);
+        vmA = (uint32_t)__ballot(iv0 >= 0);
+        vmB = (uint32_t)__ballot(iv1 >= 0);
+        vmC = (uint32_t)__ballot(iv2 >= 0);
         gload(iv0);
         lstore(tile0);
-        if (ntiles > 1) gload(iv1);
-        ivn = load_idx(2);
+        if (ntiles > 1) {
+            gload(iv1);
+            lstore(tile1);
+        }
+        if (ntiles > 2) gload(iv2);
+        ivn = load_idx(3);
     }
     __syncthreads();
-    for (int t = 0; t < ntiles; t += 2) {
-        vmE = step(tile0, tile1, vmE, t);
+    for (int t = 0; t < ntiles; t += 3) {
+        vmA = step(tile0, tile2, vmA, t);
         if (t + 1 >= ntiles) break;
-        vmO = step(tile1, tile0, vmO, t + 1);
+        vmB = step(tile1, tile0, vmB, t + 1);
+        if (t + 2 >= ntiles) break;
+        vmC = step(tile2, tile1, vmC, t + 2);
     }
 
     // Denominators: sum the per-lane shares of each head over its 32 lanes.

@@ -350,31 +350,46 @@ def run_batched(args, dev):
 
 
 def run_attention(args, dev):
-    """The composed CSA step: the indexer's top-k of the workload (default
-    W4, S = 262,144) followed by the sparse attention over the selected
-    entries (64 heads, 576-dim latent keys, their first 512 dims as values).
+    """The composed CSA step: the indexer's top-k of the workload (W4, at
+    S = 262,144, is the page's composed run) followed by the sparse attention
+    over the selected entries (64 heads, 576-dim latent keys, their first 512
+    dims as values); with --attn-random, the attention alone over a seeded
+    uniform random selection of k entries per row.
     One JSON line: per-stage times, the attention kernel against the bf16
     MFMA peak (flops of the valid selected entries only), and peak HBM over
     inputs, outputs and workspace of both stages."""
     torch.cuda.reset_peak_memory_stats(dev)
     base_alloc = torch.cuda.memory_allocated(dev)
-    c, qi, wi, kc, dist = make_inputs(args.workload, dev)
+    if args.attn_random:
+        c = inputs.config(args.workload)
+        dist = "none: every row selects k uniform random entries"
+    else:
+        c, qi, wi, kc, dist = make_inputs(args.workload, dev)
     S, T, Hi, Di, m, k = c["S"], c["T"], c["H"], c["D"], c["m"], c["k"]
     HA, DK, DV = args.attn_heads, 576, 512
     qa, kv = inputs.attention_gaussian(S, T, HA, DK, seed=1000 + args.workload, device=dev)
-    ws_bytes = csa.workspace_size(S, T, Hi, Di, m, k, chunk_keys=args.chunk, key_tile=args.tile,
-                                  workspace_budget=args.budget)
-    workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
-    idx = torch.empty((S, k), dtype=torch.int32, device=dev)
-    score = torch.empty((S, k), dtype=torch.float32, device=dev)
     out = torch.empty((S, HA, DV), dtype=torch.bfloat16, device=dev)
-    kw = dict(chunk_keys=args.chunk, key_tile=args.tile, workspace_budget=args.budget,
-              workspace=workspace, out=(idx, score))
     scale = 1.0 / DK ** 0.5
+    if args.attn_random:
+        ws_bytes = 0
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2000 + args.workload)
+        idx = torch.randint(0, T, (S, k), generator=gen, device=dev, dtype=torch.int32)
 
-    def step():
-        csa.topk(qi, wi, kc, m, k, **kw)
-        csa.sparse_attention(qa, kv, idx, DV, scale=scale, out=out)
+        def step():
+            csa.sparse_attention(qa, kv, idx, DV, scale=scale, out=out)
+    else:
+        ws_bytes = csa.workspace_size(S, T, Hi, Di, m, k, chunk_keys=args.chunk,
+                                      key_tile=args.tile, workspace_budget=args.budget)
+        workspace = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+        idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+        score = torch.empty((S, k), dtype=torch.float32, device=dev)
+        kw = dict(chunk_keys=args.chunk, key_tile=args.tile, workspace_budget=args.budget,
+                  workspace=workspace, out=(idx, score))
+
+        def step():
+            csa.topk(qi, wi, kc, m, k, **kw)
+            csa.sparse_attention(qa, kv, idx, DV, scale=scale, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -389,15 +404,19 @@ def run_attention(args, dev):
     csa.profile_enable(False)
     prof = csa.profile_collect()
     ms = (t1 - t0) * 1e3 / args.steps
-    n = np.minimum(T, (np.arange(S, dtype=np.int64) + 1) // m)
-    entries = int(np.minimum(n, k).sum())           # valid selected entries
+    if args.attn_random:
+        entries = S * k
+    else:
+        n = np.minimum(T, (np.arange(S, dtype=np.int64) + 1) // m)
+        entries = int(np.minimum(n, k).sum())       # valid selected entries
     flops = entries * HA * (DK + DV) * 2
     att_ms = prof["attention"][0] / max(prof["attention"][1], 1)
     achieved = flops / (att_ms * 1e-3) / 1e12
     gathered = entries * DK * 2
     peak = torch.cuda.max_memory_allocated(dev) - base_alloc
     print(json.dumps({
-        "mode": "composed indexer + sparse attention", "workload": args.workload,
+        "mode": ("sparse attention over a random selection" if args.attn_random
+                 else "composed indexer + sparse attention"), "workload": args.workload,
         "config": {"S": S, "T": T, "H_I": Hi, "D_I": Di, "m": m, "k": k,
                    "attention_heads": HA, "latent_dim": DK, "value_dim": DV,
                    "indexer_inputs": dist, "attention_inputs": "q, kv ~ N(0,1) bf16"},
@@ -539,6 +558,9 @@ def main():
                     help="time the composed step: the workload's indexer top-k, then the sparse "
                          "attention over the selected entries (one JSON line)")
     ap.add_argument("--attn-heads", type=int, default=64, help="attention heads (32 or 64)")
+    ap.add_argument("--attn-random", action="store_true",
+                    help="with --attention: time the attention alone over a seeded uniform random "
+                         "selection of k entries for every row (no indexer stage)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="bytes of a plain device copy run once before timing, as a known "
                          "reference for HBM traffic counters")

@@ -17,13 +17,14 @@
 // keeps its heads' q for k-steps qq*KQ .. qq*KQ+KQ-1 resident (a quarter of
 // dk), so every wave of a head block computes a partial 32x32 logit block per
 // 32-entry tile with v_mfma_f32_32x32x16_bf16; the four partials meet in LDS.
-// The selected latent rows are gathered into registers (each lane fetches
-// the 16 bytes its slot of the swizzled tile needs, straight from the row
-// the index names; -1 reads zeros through the buffer range check) a tile
-// ahead and written into the free one of three static LDS tile buffers
-// under the next tile's MFMAs.  (An LDS DMA gather would need no registers,
-// but every barrier waits for all DMAs in flight, which would leave it half
-// a tile.)  Per tile:
+// The selected latent rows are gathered by LDS DMA into the free one of
+// three static tile buffers: each lane moves the 16 bytes its slot of the
+// swizzled tile needs, straight from the row the index names (-1 reads
+// zeros through the buffer range check).  The gather of tile t+2 starts
+// after the first barrier of tile t and has until the second barrier of
+// tile t+1; the barriers inside the loop carry no memory fence (a fence
+// would wait for every DMA in flight), and the wait for a tile's DMAs is
+// an explicit vmcnt before the barrier that publishes it.  Per tile:
 //   1. partial logits (MFMA, B fragments from the tile),
 //   2. barrier; wave qq of a head block finishes 8 of its 32 heads: sums the
 //      partials in a fixed order, masks padding, takes the tile max and runs
@@ -87,6 +88,42 @@ __device__ inline float half_max(float x)
     return (threadIdx.x & 32) ? hi : lo;
 }
 
+// Barrier without a memory fence: the compiler's fence would also wait for
+// every LDS DMA in flight.  The wave's own LDS accesses are complete after
+// lgkmcnt(0); the "memory" clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ inline void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// P fragment read written as asm (with its own wait): as a plain load, the
+// compiler's wait placement puts a wait for every DMA in flight before it.
+__device__ inline bf16x8 lds_read_p(const __bf16 *p)
+{
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+    bf16x8 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    return v;
+}
+
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt left alone), as the builtin so that
+// the compiler's own wait placement knows about it.
+template <int N>
+__device__ inline void vm_wait()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One 16-byte LDS DMA per lane: bytes [off, off+16) of the buffer land at
+// dst + 16*lane (dst wave-uniform).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)dst, 16,
+                                            off, 0, 0, 0);
+}
+
 template <int DK, int DV, int HB>
 __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
 {
@@ -103,11 +140,14 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) unsigned char tile0[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char tile1[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char tile2[TILEB];
-    __shared__ __attribute__((aligned(16))) f32x4 part[WAVES][4][64];  // [wave][row quad][lane]
+    // part[w][r-1]: quad r (r = 1..3) of wave w's partial logits, for the
+    // wave of its head block that finishes those heads.
+    __shared__ __attribute__((aligned(16))) f32x4 part[WAVES][3][64];
     __shared__ __attribute__((aligned(16))) __bf16 pbuf[HB * 32][kPRow];
     __shared__ __attribute__((aligned(16))) float alpha_s[HB * 32];
     __shared__ __attribute__((aligned(16))) float l_s[HB * 32];
     __shared__ int flag_s[WAVES];
+    __shared__ __attribute__((aligned(16))) unsigned char sink[1024];  // target of the spare DMAs
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -119,45 +159,60 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     const int ntiles = (k + kTile - 1) / kTile;
     const int32_t *irow = a.idx + row * (int64_t)k;
 
-    // Resident q: head hb*32+col, dims (qq*KQ + j)*16 + half*8 .. +7.
+    // Resident q, heads rotated by 8*qq: A row r of this wave is head
+    // hb*32 + (r + 8qq) % 32, so accumulator quad 0 (rows 4half .. 4half+3)
+    // holds the heads this wave finishes (8qq + 4half + ii) and quad r the
+    // heads of wave (qq + r) % 4.  Dims (qq*KQ + j)*16 + half*8 .. +7.
     bf16x8 qf[KQ];
     {
-        const __bf16 *qh = (const __bf16 *)a.q + ((int64_t)row * a.H + hb * 32 + col) * DK;
+        const int head = hb * 32 + ((col + 8 * qq) & 31);
+        const __bf16 *qh = (const __bf16 *)a.q + ((int64_t)row * a.H + head) * DK;
 #pragma unroll
         for (int j = 0; j < KQ; ++j) qf[j] = *(const bf16x8 *)(qh + (qq * KQ + j) * 16 + half * 8);
     }
+    // Wait for q here, ahead of the gather loads: otherwise the compiler
+    // may place that wait in the tile loop, where it also waits for the
+    // gather loads in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // Entry index of tile row (lane % 32) of tile t, -1 past k.
-    auto load_idx = [&](int t) -> int {
-        const int e = t * kTile + col;
-        return (t < ntiles && e < k) ? irow[e] : -1;
-    };
+    // Entry index of tile row (lane % 32) of tile t; rows past k read the
+    // last index (a valid address) and are masked where used.
+    auto load_idx = [&](int t) -> int { return irow[min(t * kTile + col, k - 1)]; };
     // Gather of one tile: piece p of the tile is 1 KiB; its lane l holds
     // bytes [16l, 16l+16) of the piece, i.e. row r, slot s of the tile,
     // which is chunk s ^ (r % 8) of latent row idx[r] (the swizzle spreads a
-    // B-fragment read over the banks).
+    // B-fragment read over the banks).  Per piece the lane's row (as a
+    // bpermute byte address) and chunk byte offset are fixed for the row.
     const __amdgpu_buffer_rsrc_t kv_rs = buffer_rsrc(a.kv, (uint32_t)(a.T * ROWB));
-    u32x4 st[PPW];
-    auto gload = [&](int iv) {
+    int g_row[PPW], g_chunk[PPW];
+#pragma unroll
+    for (int j = 0; j < PPW; ++j) {
+        const int pos = (j * WAVES + wave) * 1024 + lane * 16;
+        const int r = (pos / ROWB) & 31;  // pieces past the tile (p >= NPIECE) go to the sink
+        g_row[j] = r * 4;
+        g_chunk[j] = (((pos % ROWB) >> 4) ^ (r & 7)) * 16;
+    }
+    // DMA gather of tile t into dst, rows from iv (idx of tile t).  Every
+    // wave issues exactly PPW DMAs per call, whatever t: pieces past the
+    // tile go to the sink, rows past k (all of them for t >= ntiles) read
+    // zeros, so the count of memory ops in flight is the same on every
+    // path and the waits can count on it.
+    auto gdma = [&](unsigned char *dst, int iv, int t) {
+        const int lim = k - t * kTile;  // rows r >= lim are past k
+        int e[PPW];
+#pragma unroll
+        for (int j = 0; j < PPW; ++j) e[j] = __builtin_amdgcn_ds_bpermute(g_row[j], iv);
 #pragma unroll
         for (int j = 0; j < PPW; ++j) {
             const int p = j * WAVES + wave;
-            const int pos = p * 1024 + lane * 16;
-            const int r = (pos / ROWB) & 31;  // pieces past the tile (p >= NPIECE) are never stored
-            const int chunk = ((pos % ROWB) >> 4) ^ (r & 7);
-            const int e = __shfl(iv, r);
-            const int off = e >= 0 ? e * ROWB + chunk * 16 : (int)0x80000000;
-            st[j] = __builtin_amdgcn_raw_buffer_load_b128(kv_rs, off, 0, 0);
+            const bool in_tile = p < NPIECE;  // wave-uniform
+            // A negative index, a row past k or a spare piece gets bit 31
+            // set: out of the buffer's range, so the DMA writes zeros.
+            const int past = ((g_row[j] >> 2) >= lim || !in_tile) ? (int)0x80000000 : 0;
+            const int off = (e[j] * ROWB + g_chunk[j]) | (e[j] & (int)0x80000000) | past;
+            dma16(kv_rs, in_tile ? dst + p * 1024 : sink, off);
         }
     };
-    auto lstore = [&](unsigned char *dst) {
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) {
-            const int p = j * WAVES + wave;
-            if (p < NPIECE) *(u32x4 *)(dst + p * 1024 + lane * 16) = st[j];  // wave-uniform test
-        }
-    };
-
     f32x16 o[NBW];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) o[nb] = f32x16{};
@@ -168,7 +223,6 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         lsum[ii] = 0.0f;
     }
     const float c2 = a.scale_log2e;
-    int ivn = -1;  // entry indices of the next tile to gather
 
     // Per-lane byte offsets inside a tile, fixed for the whole row.
     // Logit B fragments: entry col, chunk 2*(qq*KQ + j) + half, swizzled.
@@ -197,11 +251,11 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         }
     }
 
-    // Tile t in buffer tb (published by the barriers of tile t-1); store:
-    // the buffer that receives tile t+2 from the staging registers; vmask:
-    // which rows of tile t hold an entry.  Returns the row mask of tile t+3,
-    // whose gather it starts.
-    auto step = [&](const unsigned char *tb, unsigned char *store, uint32_t vmask, int t) -> uint32_t {
+    // Tile t in buffer tb (published by the barrier before this step); dst:
+    // the buffer that receives tile t+2 (its last readers, tile t-1's, are
+    // done once this step's first barrier is passed); ivc: idx of tile t,
+    // replaced by idx of tile t+3; ivd: idx of tile t+2.
+    auto step = [&](const unsigned char *tb, unsigned char *dst, int &ivc, int ivd, int t) {
         // 1. partial logits of head block hb over this wave's quarter of dk.
         f32x16 acc = {};
 #pragma unroll
@@ -210,20 +264,19 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], b, acc, 0, 0, 0);
         }
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-            if (r4 != qq)  // this wave reduces its own quarter from registers
-                part[wave][r4][lane] = f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
-        __syncthreads();
-        // 2. heads 8qq + 4half + ii (accumulator rows 4qq + ii), entry col.
-        // Partials summed in wave order (a fixed order for every quarter).
-        f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int r4 = 1; r4 < 4; ++r4)  // quad 0 stays: this wave finishes those heads
+            part[wave][r4 - 1][lane] = f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
+        lds_barrier();
+        // The gather of tile t+2 (into the buffer of tile t-1) starts here;
+        // the barrier before step t+2 waits for it.
+        const uint32_t vmask = (uint32_t)__ballot(ivc >= 0 && t * kTile + col < k);
+        ivc = load_idx(t + 3);
+        gdma(dst, ivd, t + 2);
+        // 2. heads 8qq + 4half + ii (accumulator quad 0), entry col: the own
+        // quarter, then those of waves qq+1, qq+2, qq+3 (a fixed order).
+        f32x4 s = f32x4{acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-            f32x4 pw;
-            if (w2 == qq) pw = f32x4{acc[4 * qq], acc[4 * qq + 1], acc[4 * qq + 2], acc[4 * qq + 3]};
-            else pw = part[hb * 4 + w2][qq][lane];
-            s = w2 == 0 ? pw : s + pw;
-        }
+        for (int d = 1; d < 4; ++d) s += part[hb * 4 + ((qq + d) & 3)][3 - d][lane];
         const bool valid = (vmask >> col) & 1u;
         float x[4];
         bool exceed = false;
@@ -261,17 +314,11 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
             pbuf[hb * 32 + 8 * qq + 4 * half + ii][col] = (__bf16)p;
         }
         if (lane == 0) flag_s[wave] = wave_need ? 1 : 0;
-        __syncthreads();
-        // Tile t+2 into the buffer of tile t-1 (its last readers finished
-        // before this tile's first barrier), then the gather of tile t+3
-        // into the freed registers; both run under the MFMAs below.
-        if (t + 2 < ntiles) lstore(store);
-        uint32_t vm3 = 0;
-        if (t + 3 < ntiles) {
-            vm3 = (uint32_t)__ballot(ivn >= 0);
-            gload(ivn);
-            ivn = load_idx(t + 4);
-        }
+        // Tile t+1 (gathered during step t-1) must be in LDS before this
+        // barrier: wait until at most the ops issued after its DMAs (the
+        // idx load and the DMAs of tile t+2 above) are in flight.
+        vm_wait<PPW + 1>();
+        lds_barrier();
         // 3. O = alpha * O + P V for head block hb, dims qq*DV/4 .. +DV/4-1.
         const bool resc = (flag_s[hb * 4] | flag_s[hb * 4 + 1] | flag_s[hb * 4 + 2] |
                            flag_s[hb * 4 + 3]) != 0;  // block-uniform
@@ -287,7 +334,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 pa = *(const bf16x8 *)&pbuf[hb * 32 + col][kk * 16 + half * 8];
+            const bf16x8 pa = lds_read_p(&pbuf[hb * 32 + col][kk * 16 + half * 8]);
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
                 const int hi = ((cq + nb * 4) & ~7) * 16;  // wave-uniform
@@ -299,34 +346,28 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
                                                                 o[nb], 0, 0, 0);
             }
         }
-        return vm3;
     };
 
-    // Tiles rotate through the three buffers (the loop is unrolled by three
-    // so that every access names its buffer), and so do the row masks.
-    uint32_t vmA = 0, vmB = 0, vmC = 0;
+    // Tiles rotate through the three buffers and three idx registers (the
+    // loop is unrolled by three so that every access names its buffer).
+    int iv0 = -1, iv1 = -1, iv2 = -1;
     if (ntiles > 0) {
-        const int iv0 = load_idx(0), iv1 = load_idx(1), iv2 = load_idx(2);
-        vmA = (uint32_t)__ballot(iv0 >= 0);
-        vmB = (uint32_t)__ballot(iv1 >= 0);
-        vmC = (uint32_t)__ballot(iv2 >= 0);
-        gload(iv0);
-        lstore(tile0);
-        if (ntiles > 1) {
-            gload(iv1);
-            lstore(tile1);
-        }
-        if (ntiles > 2) gload(iv2);
-        ivn = load_idx(3);
+        iv0 = load_idx(0);
+        iv1 = load_idx(1);
+        iv2 = load_idx(2);
+        gdma(tile0, iv0, 0);
+        gdma(tile1, iv1, 1);
+        vm_wait<0>();
     }
     __syncthreads();
     for (int t = 0; t < ntiles; t += 3) {
-        vmA = step(tile0, tile2, vmA, t);
+        step(tile0, tile2, iv0, iv2, t);
         if (t + 1 >= ntiles) break;
-        vmB = step(tile1, tile0, vmB, t + 1);
+        step(tile1, tile0, iv1, iv0, t + 1);
         if (t + 2 >= ntiles) break;
-        vmC = step(tile2, tile1, vmC, t + 2);
+        step(tile2, tile1, iv2, iv1, t + 2);
     }
+    __syncthreads();
 
     // Denominators: sum the per-lane shares of each head over its 32 lanes.
 #pragma unroll

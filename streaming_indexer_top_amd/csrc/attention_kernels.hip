@@ -190,7 +190,9 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         const int pos = (j * WAVES + wave) * 1024 + lane * 16;
         const int r = (pos / ROWB) & 31;  // pieces past the tile (p >= NPIECE) go to the sink
         g_row[j] = r * 4;
-        g_chunk[j] = (((pos % ROWB) >> 4) ^ (r & 7)) * 16;
+        // Spare pieces (the sink's) get an offset that is out of range for
+        // any real row.
+        g_chunk[j] = j * WAVES + wave < NPIECE ? (((pos % ROWB) >> 4) ^ (r & 7)) * 16 : (int)0x80000000;
     }
     // DMA gather of tile t into dst, rows from iv (idx of tile t).  Every
     // wave issues exactly PPW DMAs per call, whatever t: pieces past the
@@ -199,27 +201,29 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     // path and the waits can count on it.
     auto gdma = [&](unsigned char *dst, int iv, int t) {
         const int lim = k - t * kTile;  // rows r >= lim are past k
+        // Byte offset of this lane's row (lane % 32); a negative index, or a
+        // row past k, gets bit 31: out of the buffer's range, so the DMAs of
+        // that row write zeros.
+        const int eoff = (iv >= 0 && col < lim) ? iv * ROWB : (int)0x80000000;
         int e[PPW];
 #pragma unroll
-        for (int j = 0; j < PPW; ++j) e[j] = __builtin_amdgcn_ds_bpermute(g_row[j], iv);
+        for (int j = 0; j < PPW; ++j) e[j] = __builtin_amdgcn_ds_bpermute(g_row[j], eoff);
 #pragma unroll
         for (int j = 0; j < PPW; ++j) {
             const int p = j * WAVES + wave;
-            const bool in_tile = p < NPIECE;  // wave-uniform
-            // A negative index, a row past k or a spare piece gets bit 31
-            // set: out of the buffer's range, so the DMA writes zeros.
-            const int past = ((g_row[j] >> 2) >= lim || !in_tile) ? (int)0x80000000 : 0;
-            const int off = (e[j] * ROWB + g_chunk[j]) | (e[j] & (int)0x80000000) | past;
-            dma16(kv_rs, in_tile ? dst + p * 1024 : sink, off);
+            dma16(kv_rs, p < NPIECE ? dst + p * 1024 : sink, e[j] + g_chunk[j]);
         }
     };
     f32x16 o[NBW];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) o[nb] = f32x16{};
-    float mref[4], lsum[4];  // reference max and per-lane denominators of heads 8qq+4half+ii
+    // Reference max, the threshold mref + kTau and the per-lane denominators
+    // of heads 8qq + 4half + ii.
+    float mref[4], thr[4], lsum[4];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         mref[ii] = -__builtin_inff();
+        thr[ii] = -__builtin_inff();
         lsum[ii] = 0.0f;
     }
     const float c2 = a.scale_log2e;
@@ -282,9 +286,10 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         bool exceed = false;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            x[ii] = valid ? s[ii] * c2 : -__builtin_inff();
-            exceed |= x[ii] > mref[ii] + kTau;
+            x[ii] = s[ii] * c2;
+            exceed |= x[ii] > thr[ii];
         }
+        exceed = exceed && valid;
         // A head's reference max moves only when some logit of the tile
         // exceeds it by more than kTau; usually none does, and the tile
         // maxima are not needed at all.
@@ -292,11 +297,12 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         if (wave_need) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const float mx = half_max(x[ii]);
+                const float mx = half_max(valid ? x[ii] : -__builtin_inff());
                 float alpha = 1.0f;
-                if (mx > mref[ii] + kTau) {
+                if (mx > thr[ii]) {
                     alpha = __builtin_amdgcn_exp2f(mref[ii] - mx);
                     mref[ii] = mx;
+                    thr[ii] = mx + kTau;
                     lsum[ii] *= alpha;
                 }
                 if (col == 0) alpha_s[hb * 32 + 8 * qq + 4 * half + ii] = alpha;
@@ -308,8 +314,9 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         }
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-            const float p = mref[ii] == -__builtin_inff() ? 0.0f
-                                                          : __builtin_amdgcn_exp2f(x[ii] - mref[ii]);
+            // A present entry has a finite reference max (its logit set
+            // one if none was); an absent one gets 0.
+            const float p = valid ? __builtin_amdgcn_exp2f(x[ii] - mref[ii]) : 0.0f;
             lsum[ii] += p;
             pbuf[hb * 32 + 8 * qq + 4 * half + ii][col] = (__bf16)p;
         }

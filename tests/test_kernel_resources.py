@@ -84,3 +84,27 @@ def test_select_kernels_no_scratch_on_the_hot_path(select_asm):
     for name, m in meta.items():
         if "merge" in name:
             assert m["private_segment_fixed_size"] == 0 and m["vgpr_spill_count"] == 0, name
+
+
+@pytest.fixture(scope="module")
+def attention_asm(tmp_path_factory):
+    return device_asm("attention_kernels.hip", tmp_path_factory.mktemp("asm"))
+
+
+def test_attention_kernels_fit_one_row_per_cu(attention_asm):
+    """Every attention instance: no spills, no scratch, LDS within the CU's
+    160 KiB.  The 64-head instances run 8 waves (two per SIMD), so at most
+    256 registers; the 32-head ones run 4 waves (one per SIMD)."""
+    meta = kernel_meta(attention_asm)
+    att = {n: m for n, m in meta.items() if "attention_kernel" in n}
+    assert len(att) == 4
+    for name, m in att.items():
+        assert m["vgpr_spill_count"] == 0 and m["sgpr_spill_count"] == 0, name
+        assert m["private_segment_fixed_size"] == 0, name
+        assert "scratch_" not in body(attention_asm, name), name
+        if name.endswith("Li2EEEvNS_8AttnArgsE"):
+            assert m["vgpr_count"] <= 256, name
+    for block in attention_asm.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        if "attention_kernel" in name:
+            assert int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", block).group(1)) <= 160 * 1024, name

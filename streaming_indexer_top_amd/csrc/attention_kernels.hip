@@ -58,6 +58,18 @@ __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t 
                                              0x00020000);
 }
 
+// Tile swizzle: slot s of tile row r (16-byte slots, in groups of eight per
+// 128 bytes) holds chunk s ^ sw8(r) of the row.  Rows are 1152 bytes apart,
+// a multiple of 128, so without it every row would start on the same bank.
+// The map sends row bits 0, 1, 2, 3 to slot bits 1, 2, 0, 1: the logit
+// fragment read (eight or sixteen consecutive rows, one chunk each) and the
+// transposing value read (four consecutive rows, four chunks each) then hit
+// every bank once, whether the LDS serves 128 or 256 bytes a cycle.
+__device__ inline int sw8(int r)
+{
+    return ((r >> 2) & 1) | (((r ^ (r >> 3)) & 1) << 1) | (((r >> 1) & 1) << 2);
+}
+
 // Transposing LDS read: within each 16-lane group, lane o receives element
 // o%4 of the 8-byte rows that lanes o/4, o/4+4, o/4+8, o/4+12 point at.
 __device__ inline i16x4 read_tr16(const unsigned char *p)
@@ -180,7 +192,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     auto load_idx = [&](int t) -> int { return irow[min(t * kTile + col, k - 1)]; };
     // Gather of one tile: piece p of the tile is 1 KiB; its lane l holds
     // bytes [16l, 16l+16) of the piece, i.e. row r, slot s of the tile,
-    // which is chunk s ^ (r % 8) of latent row idx[r] (the swizzle spreads a
+    // which is chunk s ^ sw8(r) of latent row idx[r] (the swizzle spreads a
     // B-fragment read over the banks).  Per piece the lane's row (as a
     // bpermute byte address) and chunk byte offset are fixed for the row.
     const __amdgpu_buffer_rsrc_t kv_rs = buffer_rsrc(a.kv, (uint32_t)(a.T * ROWB));
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         g_row[j] = r * 4;
         // Spare pieces (the sink's) get an offset that is out of range for
         // any real row.
-        g_chunk[j] = j * WAVES + wave < NPIECE ? (((pos % ROWB) >> 4) ^ (r & 7)) * 16 : (int)0x80000000;
+        g_chunk[j] = j * WAVES + wave < NPIECE ? (((pos % ROWB) >> 4) ^ sw8(r)) * 16 : (int)0x80000000;
     }
     // DMA gather of tile t into dst, rows from iv (idx of tile t).  Every
     // wave issues exactly PPW DMAs per call, whatever t: pieces past the
@@ -233,13 +245,13 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     int qk_off[KQ];
 #pragma unroll
     for (int j = 0; j < KQ; ++j)
-        qk_off[j] = col * ROWB + (((2 * (qq * KQ + j) + half) ^ (col & 7)) << 4);
+        qk_off[j] = col * ROWB + (((2 * (qq * KQ + j) + half) ^ sw8(col)) << 4);
     // Value fragments read by the transposing loads: this lane points at
     // entry kk*16 + eb + 4*s2 (s2: first or second half of its 8 entries),
     // dims dl..dl+3 of output block nb; inside a tile that is byte
     //   kk*16*ROWB + hi(nb) + tr_off[s2][parity(nb)]
     // where hi(nb) is the 128-byte group of the block's chunks and the
-    // parity picks which half of that group, which the swizzle (entry % 8)
+    // parity picks which half of that group, which the swizzle (sw8(entry))
     // permutes per lane.
     const int eb = ((lane >> 5) * 8) + ((lane & 15) >> 2);
     const int dl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
 #pragma unroll
         for (int par = 0; par < 2; ++par) {
             const int bp = ((cq >> 2) + par) & 1;  // bit 2 of the block's first chunk
-            tr_off[s2][par] = e * ROWB + (((bp * 4 + (dl >> 3)) ^ (e & 7)) << 4) + (dl & 7) * 2;
+            tr_off[s2][par] = e * ROWB + (((bp * 4 + (dl >> 3)) ^ sw8(e)) << 4) + (dl & 7) * 2;
         }
     }
 

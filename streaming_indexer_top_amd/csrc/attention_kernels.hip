@@ -267,32 +267,45 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         }
     }
 
-    // Tile t in buffer tb (published by the barrier before this step); dst:
-    // the buffer that receives tile t+2 (its last readers, tile t-1's, are
-    // done once this step's first barrier is passed); ivc: idx of tile t,
-    // replaced by idx of tile t+3; ivd: idx of tile t+2.
-    auto step = [&](const unsigned char *tb, unsigned char *dst, int &ivc, int ivd, int t) {
-        // 1. partial logits of head block hb over this wave's quarter of dk.
-        f32x16 acc = {};
+    // Logits of tile t+1 are computed during the softmax of tile t: the
+    // MFMAs run while the same waves do the vector work.  acc holds them
+    // from the first interval of a step to the second; own keeps this
+    // wave's quarter of its own heads (quad 0) for the next softmax.
+    f32x16 acc = {};
+    f32x4 own = {};
+    auto qk = [&](const unsigned char *tb) {
+        acc = f32x16{};
 #pragma unroll
         for (int j = 0; j < KQ; ++j) {
             const bf16x8 b = *(const bf16x8 *)(tb + qk_off[j]);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], b, acc, 0, 0, 0);
         }
+    };
+    auto write_parts = [&]() {
+        own = f32x4{acc[0], acc[1], acc[2], acc[3]};
 #pragma unroll
         for (int r4 = 1; r4 < 4; ++r4)  // quad 0 stays: this wave finishes those heads
             part[wave][r4 - 1][lane] = f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
-        lds_barrier();
-        // The gather of tile t+2 (into the buffer of tile t-1) starts here;
-        // the barrier before step t+2 waits for it.
+    };
+
+    // Step t, two intervals.  First: the idx of tile t+3 and the gather of
+    // tile t+2 (into the buffer tile t-1 left), this wave's logit sums of
+    // tile t (own quarter, then waves qq+1, qq+2, qq+3: a fixed order), the
+    // logit MFMAs of tile t+1, and the softmax of tile t (P, factors and
+    // flag to LDS).  Second: the partial logits of tile t+1 to LDS, then
+    // O = alpha * O + P V of tile t; the gather of tile t+2 is waited for
+    // before the barrier that ends the step.  tb: tile t; tn: tile t+1;
+    // dst: the buffer of tile t+2; ivc: idx of tile t, replaced by idx of
+    // tile t+3; ivd: idx of tile t+2.
+    auto step = [&](const unsigned char *tb, const unsigned char *tn, unsigned char *dst, int &ivc,
+                    int ivd, int t) {
         const uint32_t vmask = (uint32_t)__ballot(ivc >= 0 && t * kTile + col < k);
         ivc = load_idx(t + 3);
         gdma(dst, ivd, t + 2);
-        // 2. heads 8qq + 4half + ii (accumulator quad 0), entry col: the own
-        // quarter, then those of waves qq+1, qq+2, qq+3 (a fixed order).
-        f32x4 s = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        f32x4 s = own;
 #pragma unroll
         for (int d = 1; d < 4; ++d) s += part[hb * 4 + ((qq + d) & 3)][3 - d][lane];
+        if (t + 1 < ntiles) qk(tn);
         const bool valid = (vmask >> col) & 1u;
         float x[4];
         bool exceed = false;
@@ -333,11 +346,8 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
             pbuf[hb * 32 + 8 * qq + 4 * half + ii][col] = (__bf16)p;
         }
         if (lane == 0) flag_s[wave] = wave_need ? 1 : 0;
-        // Tile t+1 (gathered during step t-1) must be in LDS before this
-        // barrier: wait until at most the ops issued after its DMAs (the
-        // idx load and the DMAs of tile t+2 above) are in flight.
-        vm_wait<PPW + 1>();
         lds_barrier();
+        if (t + 1 < ntiles) write_parts();
         // 3. O = alpha * O + P V for head block hb, dims qq*DV/4 .. +DV/4-1.
         const bool resc = (flag_s[hb * 4] | flag_s[hb * 4 + 1] | flag_s[hb * 4 + 2] |
                            flag_s[hb * 4 + 3]) != 0;  // block-uniform
@@ -365,6 +375,8 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
                                                                 o[nb], 0, 0, 0);
             }
         }
+        vm_wait<0>();
+        lds_barrier();
     };
 
     // Tiles rotate through the three buffers and three idx registers (the
@@ -379,12 +391,17 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         vm_wait<0>();
     }
     __syncthreads();
+    if (ntiles > 0) {
+        qk(tile0);
+        write_parts();
+    }
+    __syncthreads();
     for (int t = 0; t < ntiles; t += 3) {
-        step(tile0, tile2, iv0, iv2, t);
+        step(tile0, tile1, tile2, iv0, iv2, t);
         if (t + 1 >= ntiles) break;
-        step(tile1, tile0, iv1, iv0, t + 1);
+        step(tile1, tile2, tile0, iv1, iv0, t + 1);
         if (t + 2 >= ntiles) break;
-        step(tile2, tile1, iv2, iv1, t + 2);
+        step(tile2, tile0, tile1, iv2, iv1, t + 2);
     }
     __syncthreads();
 

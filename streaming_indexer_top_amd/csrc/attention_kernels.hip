@@ -20,21 +20,24 @@
 // The selected latent rows are gathered by LDS DMA into the free one of
 // three static tile buffers: each lane moves the 16 bytes its slot of the
 // swizzled tile needs, straight from the row the index names (-1 reads
-// zeros through the buffer range check).  The gather of tile t+2 starts
-// after the first barrier of tile t and has until the second barrier of
-// tile t+1; the barriers inside the loop carry no memory fence (a fence
-// would wait for every DMA in flight), and the wait for a tile's DMAs is
-// an explicit vmcnt before the barrier that publishes it.  Per tile:
-//   1. partial logits (MFMA, B fragments from the tile),
-//   2. barrier; wave qq of a head block finishes 8 of its 32 heads: sums the
-//      partials in a fixed order, masks padding, takes the tile max and runs
-//      an online softmax in base 2 whose reference max moves only when a
-//      head's max rises by more than 2^8 (the factor then rescales the
-//      accumulators; otherwise they are left alone), writes P (bf16) to LDS,
-//   3. barrier; P * V with v_mfma_f32_32x32x16_bf16, wave qq owning a quarter
-//      of the dv output dims: the V fragments (8 consecutive entries of one
-//      dim per lane) come from the row-major tile by ds_read_b64_tr_b16, two
-//      transposing 8-byte reads per fragment.
+// zeros through the buffer range check).  The gather of tile t+2 starts at
+// the beginning of tile step t and has until the end of that step.  The
+// barriers inside the loop carry no memory fence (a fence would wait for
+// every DMA in flight); the wait for a tile's DMAs is an explicit vmcnt
+// before the barrier that publishes it.  Tile step t has
+// two intervals between barriers:
+//   1. wave qq of a head block finishes 8 of its 32 heads for tile t: sums
+//      the four partial logit quarters in a fixed order, masks padding and
+//      runs an online softmax in base 2 whose reference max moves only when
+//      a head's max rises by more than 2^8 (the factor then rescales the
+//      accumulators; otherwise they are left alone), and writes P (bf16) to
+//      LDS; under this vector work the same waves' MFMAs compute the partial
+//      logits of tile t+1 (B fragments from the tile),
+//   2. the partials of tile t+1 go to LDS, and P * V of tile t runs with
+//      v_mfma_f32_32x32x16_bf16, wave qq owning a quarter of the dv output
+//      dims: the V fragments (8 consecutive entries of one dim per lane)
+//      come from the row-major tile by ds_read_b64_tr_b16, two transposing
+//      8-byte reads per fragment.
 // The softmax denominators are kept per lane and reduced once at the end.
 #include "csa_internal.h"
 

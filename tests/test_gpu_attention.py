@@ -58,8 +58,10 @@ def random_selection(rng, S, T, k, pad_frac=0.2):
 
 @pytest.mark.parametrize("H", [32, 64])
 @pytest.mark.parametrize("dims", [(576, 512), (128, 128)])
-@pytest.mark.parametrize("k", [1, 31, 32, 33, 100, 2048])
+@pytest.mark.parametrize("k", [1, 31, 32, 33, 65, 96, 100, 130, 192, 2048])
 def test_random_selections(H, dims, k):
+    """Tile counts 1..7 and 64 cover every exit point of the tile loop
+    (unrolled by three) and ragged last tiles."""
     DK, DV = dims
     S, T = 37, 3000
     say("attention H=%d dk=%d dv=%d k=%d" % (H, DK, DV, k))

@@ -206,8 +206,8 @@ int csa_profile_collect(double *ms_out, int64_t *launches_out, int32_t n_kinds);
  *   idx  [S][k]        int32  (4-byte aligned; may be NULL when k == 0)
  *   out  [S][H][D_V]   bf16   (2-byte aligned), fully overwritten
  *
- * idx entries must be -1 or in [0, T): this is what csa_indexer_topk
- * writes.  Other values are not detected; they read zeros (memory-safe).
+ * idx entries are -1 or in [0, T) (what csa_indexer_topk writes); any
+ * other value is treated like -1 (padding).
  * Logits and the softmax are fp32 (exp2 based, reference max moved lazily),
  * the weights are rounded to bf16 for the weighted sum, which accumulates in
  * fp32; out is rounded to bf16.

@@ -173,6 +173,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     const int k = a.k;
     const int ntiles = (k + kTile - 1) / kTile;
     const int32_t *irow = a.idx + row * (int64_t)k;
+    const int nkv = (int)a.T;  // an index outside [0, T) counts as padding
 
     // Resident q, heads rotated by 8*qq: A row r of this wave is head
     // hb*32 + (r + 8qq) % 32, so accumulator quad 0 (rows 4half .. 4half+3)
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         // Byte offset of this lane's row (lane % 32); a negative index, or a
         // row past k, gets bit 31: out of the buffer's range, so the DMAs of
         // that row write zeros.
-        const int eoff = (iv >= 0 && col < lim) ? iv * ROWB : (int)0x80000000;
+        const int eoff = (iv >= 0 && iv < nkv && col < lim) ? iv * ROWB : (int)0x80000000;
         int e[PPW];
 #pragma unroll
         for (int j = 0; j < PPW; ++j) e[j] = __builtin_amdgcn_ds_bpermute(g_row[j], eoff);
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     // tile t+3; ivd: idx of tile t+2.
     auto step = [&](const unsigned char *tb, const unsigned char *tn, unsigned char *dst, int &ivc,
                     int ivd, int t) {
-        const uint32_t vmask = (uint32_t)__ballot(ivc >= 0 && t * kTile + col < k);
+        const uint32_t vmask = (uint32_t)__ballot(ivc >= 0 && ivc < nkv && t * kTile + col < k);
         ivc = load_idx(t + 3);
         gdma(dst, ivd, t + 2);
         f32x4 s = own;

@@ -132,3 +132,23 @@ def test_repeat_runs_bit_identical():
     b = csa.sparse_attention(q, kv, idx, DV)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_out_of_range_indices_count_as_padding():
+    """Indices outside [0, T) (other than -1) are treated like -1: the
+    output equals, bit for bit, that of the same selection with those
+    entries set to -1, which in turn matches the oracle."""
+    S, T, H, DK, DV, k = 9, 500, 64, 576, 512, 70
+    say("attention out-of-range indices")
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=31)
+    rng = np.random.default_rng(31)
+    idx = rng.integers(0, T, (S, k)).astype(np.int32)
+    bad = rng.random((S, k)) < 0.2
+    junk = rng.choice(np.array([-7, -2**31, T, T + 1, 2**31 - 1], dtype=np.int64), size=(S, k))
+    idx_bad = np.where(bad, junk, idx).astype(np.int32)
+    idx_pad = np.where(bad, -1, idx).astype(np.int32)
+    o_bad = csa.sparse_attention(q.to(DEV), kv.to(DEV), torch.from_numpy(idx_bad).to(DEV), DV)
+    o_pad = csa.sparse_attention(q.to(DEV), kv.to(DEV), torch.from_numpy(idx_pad).to(DEV), DV)
+    torch.cuda.synchronize()
+    assert torch.equal(o_bad.cpu(), o_pad.cpu())
+    run_and_check(q, kv, torch.from_numpy(idx_pad), DV, 1.0 / DK ** 0.5)

@@ -455,7 +455,14 @@ __device__ __forceinline__ void sort_keys(uint64_t *cand, int nA, int nB, uint32
             const uint32_t wd = bk[bkt[i]];
             const int o = (int)(wd >> 16), m = (int)(wd & 0xFFFFu);
             int rk = 0;
-            for (int q = o; q < o + m; ++q) rk += cand[q] > key[i] ? 1 : 0;
+            int q = o;
+            // Four independent reads per round (the loop is bound by LDS
+            // latency), then the rest one by one.
+            for (; q + 3 < o + m; q += 4) {
+                const uint64_t c0 = cand[q], c1 = cand[q + 1], c2 = cand[q + 2], c3 = cand[q + 3];
+                rk += (c0 > key[i] ? 1 : 0) + (c1 > key[i] ? 1 : 0) + (c2 > key[i] ? 1 : 0) + (c3 > key[i] ? 1 : 0);
+            }
+            for (; q < o + m; ++q) rk += cand[q] > key[i] ? 1 : 0;
             pos[i] = (uint32_t)(o + rk);
         }
     }

@@ -152,3 +152,48 @@ def test_out_of_range_indices_count_as_padding():
     torch.cuda.synchronize()
     assert torch.equal(o_bad.cpu(), o_pad.cpu())
     run_and_check(q, kv, torch.from_numpy(idx_pad), DV, 1.0 / DK ** 0.5)
+
+
+def test_composed_step_hip_graph_replays_match_eager():
+    """Both calls enqueue only kernel launches on the caller's stream (no
+    allocation, no memset), so the composed step, indexer then attention,
+    can be captured in one HIP graph.  Every replay, with eager work in
+    between and the outputs and workspace scribbled over first, equals the
+    eager result bit for bit."""
+    S, T, Hi, Di, m, k = 512, 256, 64, 128, 4, 96
+    H, DK, DV = 64, 576, 512
+    say("attention composed step in a HIP graph")
+    qi, wi, kc = [t.to(DEV) for t in inputs.bf16_gaussian(S, T, Hi, Di, seed=41)]
+    q, kv = [t.to(DEV) for t in inputs.attention_gaussian(S, T, H, DK, seed=42)]
+    ws = torch.empty((max(csa.workspace_size(S, T, Hi, Di, m, k), 1),), dtype=torch.uint8, device=DEV)
+    idx = torch.empty((S, k), dtype=torch.int32, device=DEV)
+    sc = torch.empty((S, k), dtype=torch.float32, device=DEV)
+    out = torch.empty((S, H, DV), dtype=torch.bfloat16, device=DEV)
+    e_idx, _ = csa.topk(qi, wi, kc, m, k)
+    e_out = csa.sparse_attention(q, kv, e_idx, DV)
+    torch.cuda.synchronize()
+
+    def step():
+        csa.topk(qi, wi, kc, m, k, workspace=ws, out=(idx, sc))
+        csa.sparse_attention(q, kv, idx, DV, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        idx.fill_(-1)
+        out.fill_(7.0)
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, e_idx), "replay %d" % rep
+        assert torch.equal(out.view(torch.int16), e_out.view(torch.int16)), "replay %d" % rep
+        _ = (q.float() * 2).sum()  # eager work between replays
+        torch.cuda.synchronize()

@@ -112,14 +112,20 @@ __device__ inline void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// P fragment read written as asm (with its own wait): as a plain load, the
-// compiler's wait placement puts a wait for every DMA in flight before it.
-__device__ inline bf16x8 lds_read_p(const __bf16 *p)
+// The head block's four rescale flags and both P fragments of a tile, read
+// in one asm block with its own wait: as plain loads, the compiler's wait
+// placement puts a wait for every DMA in flight before them, and one wait
+// for all three saves an LDS round trip before the P * V MFMAs.
+__device__ inline void lds_read_fp(const int *f, const __bf16 *p0, const __bf16 *p1, u32x4 &fl,
+                                   bf16x8 &a0, bf16x8 &a1)
 {
-    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-    bf16x8 v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-    return v;
+    const uint32_t af = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)f;
+    const uint32_t b0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p0;
+    const uint32_t b1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p1;
+    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(fl), "=&v"(a0), "=&v"(a1)
+                 : "v"(af), "v"(b0), "v"(b1)
+                 : "memory");
 }
 
 // s_waitcnt vmcnt(N) (expcnt, lgkmcnt left alone), as the builtin so that
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) __bf16 pbuf[HB * 32][kPRow];
     __shared__ __attribute__((aligned(16))) float alpha_s[HB * 32];
     __shared__ __attribute__((aligned(16))) float l_s[HB * 32];
-    __shared__ int flag_s[WAVES];
+    __shared__ __attribute__((aligned(16))) int flag_s[WAVES];
     __shared__ __attribute__((aligned(16))) unsigned char sink[1024];  // target of the spare DMAs
 
     const int tid = threadIdx.x;
@@ -353,8 +359,11 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         lds_barrier();
         if (t + 1 < ntiles) write_parts();
         // 3. O = alpha * O + P V for head block hb, dims qq*DV/4 .. +DV/4-1.
-        const bool resc = (flag_s[hb * 4] | flag_s[hb * 4 + 1] | flag_s[hb * 4 + 2] |
-                           flag_s[hb * 4 + 3]) != 0;  // block-uniform
+        u32x4 fl;
+        bf16x8 pab[2];
+        lds_read_fp(&flag_s[hb * 4], &pbuf[hb * 32 + col][half * 8], &pbuf[hb * 32 + col][16 + half * 8], fl,
+                    pab[0], pab[1]);
+        const bool resc = __builtin_amdgcn_readfirstlane((int)(fl[0] | fl[1] | fl[2] | fl[3])) != 0;  // block-uniform
         if (resc) {
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) {
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 pa = lds_read_p(&pbuf[hb * 32 + col][kk * 16 + half * 8]);
+            const bf16x8 pa = pab[kk];
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
                 const int hi = ((cq + nb * 4) & ~7) * 16;  // wave-uniform

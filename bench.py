@@ -527,6 +527,36 @@ def run_gemm_probe(args, dev):
                       "tflops": tflops, "frac_of_2500": tflops / 2500.0}))
 
 
+def run_mfma_probe(args, dev):
+    """The register-only MFMA probe of the library (csa_probe_mfma): 2048
+    workgroups (8 per CU) of bf16 32x32x16 MFMA chains on pseudo-random
+    register operands, timed with CUDA events on torch's stream, with one
+    operand pair and with operands changing on every issue.  The rate
+    against the nominal peak is the ceiling that the matrix pipe's own power
+    draw leaves any bf16 contraction on this chip; the implied clock assumes
+    1024 flops per cycle per SIMD (1024 SIMDs)."""
+    blocks, iters = 2048, 20000
+    flops = blocks * 4 * iters * 4 * 32768.0
+    out = torch.empty((blocks * 256,), dtype=torch.float32, device=dev)
+    for rotate in (False, True):
+        for _ in range(max(args.warmup, 1)):
+            csa.probe_mfma(blocks, iters, rotate, out=out)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            csa.probe_mfma(blocks, iters, rotate, out=out)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        tflops = flops / (ms * 1e-3) / 1e12
+        print(json.dumps({"probe": "mfma_bf16_registers_only", "operands_change_every_issue": rotate,
+                          "workgroups": blocks, "mfma_per_wave": iters * 4, "steps": args.steps,
+                          "ms_per_launch": ms, "tflops": tflops, "frac_of_2500": tflops / 2500.0,
+                          "implied_clock_ghz": tflops * 1e12 / (1024.0 * 1024.0) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -572,6 +602,9 @@ def main():
                          "SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE; no GPU")
     ap.add_argument("--kernel-match", default="score_bf16_kernel",
                     help="with --mfma-busy-from: summarize the kernels whose name contains this")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="time the library's register-only MFMA probe (the bf16 matrix-pipe ceiling "
+                         "under its own power draw), one JSON line per operand mode")
     ap.add_argument("--gemm-probe", type=int, default=0,
                     help="time a plain library bf16 GEMM (torch.matmul, N x N x N) as a "
                          "reference for the MFMA rate this chip sustains; one JSON line")
@@ -596,6 +629,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.mfma_probe:
+        run_mfma_probe(args, dev)
+        return
     if args.gemm_probe:
         run_gemm_probe(args, dev)
         return

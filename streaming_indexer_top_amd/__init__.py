@@ -8,4 +8,5 @@ over its selected entries.  ``inputs`` holds the seeded synthetic input
 generators.
 """
 from .binding import (CsaError, abi_version, library_path, load_library,  # noqa: F401
-                      profile_collect, profile_enable, sparse_attention, topk, workspace_size)
+                      probe_mfma, profile_collect, profile_enable, sparse_attention, topk,
+                      workspace_size)

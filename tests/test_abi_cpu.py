@@ -207,3 +207,16 @@ def test_sparse_attention_null_and_alignment_checks():
     # No rows: nothing to do, nothing touched.
     assert lib.csa_sparse_attention(z, z, z, z, binding.CSA_BF16, 0, 10, 64, 576, 512, 8,
                                     0.1, None) == 0
+
+
+def test_mfma_probe_argument_checks():
+    """The register-only MFMA probe refuses bad sizes and NULL before any
+    HIP call."""
+    lib = csa.load_library()
+    p, z = ctypes.c_void_p(256), ctypes.c_void_p(0)
+    assert lib.csa_probe_mfma(z, 8, 16, 1, None) == 1
+    assert lib.csa_probe_mfma(p, 0, 16, 1, None) == 2
+    assert lib.csa_probe_mfma(p, (1 << 20) + 1, 16, 1, None) == 2
+    assert lib.csa_probe_mfma(p, 8, 6, 1, None) == 2
+    assert lib.csa_probe_mfma(p, 8, 0, 1, None) == 2
+    assert lib.csa_probe_mfma(ctypes.c_void_p(258), 8, 16, 1, None) == 4

@@ -541,3 +541,15 @@ def test_cfg4_mixture_sampled():
 @pytest.mark.slow
 def test_cfg5_sampled():
     _full_shape_check(5, sample=256, shard_tail=8192)
+
+
+def test_mfma_probe_runs_and_is_deterministic():
+    """The register-only MFMA probe (a measurement aid) runs through the C
+    ABI, writes one finite float per thread, and repeats bit for bit."""
+    a = csa.probe_mfma(8, 16, rotate=True)
+    b = csa.probe_mfma(8, 16, rotate=True)
+    c = csa.probe_mfma(8, 16, rotate=False)
+    torch.cuda.synchronize()
+    assert a.shape == (8 * 256,)
+    assert torch.isfinite(a).all() and torch.isfinite(c).all()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))

@@ -30,9 +30,10 @@
 //      the four partial logit quarters in a fixed order, masks padding and
 //      runs an online softmax in base 2 whose reference max moves only when
 //      a head's max rises by more than 2^8 (the factor then rescales the
-//      accumulators; otherwise they are left alone), and writes P (bf16) to
-//      LDS; under this vector work the same waves' MFMAs compute the partial
-//      logits of tile t+1 (B fragments from the tile),
+//      accumulators; otherwise they are left alone), and writes P (bf16,
+//      transposed: one 8-byte store per lane) to LDS; under this vector
+//      work the same waves' MFMAs compute the partial logits of tile t+1
+//      (B fragments from the tile),
 //   2. the partials of tile t+1 go to LDS, and P * V of tile t runs with
 //      v_mfma_f32_32x32x16_bf16, wave qq owning a quarter of the dv output
 //      dims: the V fragments (8 consecutive entries of one dim per lane)
@@ -53,7 +54,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 32;      // selected entries per tile
 constexpr float kTau = 8.0f;   // a head's reference max moves when its max rises by more than this (log2 units)
-constexpr int kPRow = 40;      // P row stride in bf16 elements (32 entries + padding against bank conflicts)
+constexpr int kPRow = 36;      // P^T row stride in bf16 elements (32 heads + padding against bank conflicts)
 
 __device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
 {
@@ -112,19 +113,22 @@ __device__ inline void lds_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// The head block's four rescale flags and both P fragments of a tile, read
-// in one asm block with its own wait: as plain loads, the compiler's wait
-// placement puts a wait for every DMA in flight before them, and one wait
-// for all three saves an LDS round trip before the P * V MFMAs.
-__device__ inline void lds_read_fp(const int *f, const __bf16 *p0, const __bf16 *p1, u32x4 &fl,
-                                   bf16x8 &a0, bf16x8 &a1)
+// The head block's four rescale flags and both P fragments of a tile (four
+// transposing 8-byte reads of P^T, as for the value fragments), read in one
+// asm block with its own wait: as plain loads, the compiler's wait placement
+// puts a wait for every DMA in flight before them, and one wait for all of
+// them saves an LDS round trip before the P * V MFMAs.
+__device__ inline uint32_t lds_addr(const void *p)
 {
-    const uint32_t af = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)f;
-    const uint32_t b0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p0;
-    const uint32_t b1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p1;
-    asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
-                 : "=&v"(fl), "=&v"(a0), "=&v"(a1)
-                 : "v"(af), "v"(b0), "v"(b1)
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+__device__ inline void lds_read_fp(const int *f, const __bf16 *p00, const __bf16 *p01, const __bf16 *p10,
+                                   const __bf16 *p11, u32x4 &fl, i16x4 &t00, i16x4 &t01, i16x4 &t10, i16x4 &t11)
+{
+    asm volatile("ds_read_b128 %0, %5\n\tds_read_b64_tr_b16 %1, %6\n\tds_read_b64_tr_b16 %2, %7\n\t"
+                 "ds_read_b64_tr_b16 %3, %8\n\tds_read_b64_tr_b16 %4, %9\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(fl), "=&v"(t00), "=&v"(t01), "=&v"(t10), "=&v"(t11)
+                 : "v"(lds_addr(f)), "v"(lds_addr(p00)), "v"(lds_addr(p01)), "v"(lds_addr(p10)), "v"(lds_addr(p11))
                  : "memory");
 }
 
@@ -164,7 +168,9 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
     // part[w][r-1]: quad r (r = 1..3) of wave w's partial logits, for the
     // wave of its head block that finishes those heads.
     __shared__ __attribute__((aligned(16))) f32x4 part[WAVES][3][64];
-    __shared__ __attribute__((aligned(16))) __bf16 pbuf[HB * 32][kPRow];
+    // P transposed: pT[hb][entry][head], read as the A fragments of P * V
+    // by the same transposing loads as the value fragments.
+    __shared__ __attribute__((aligned(16))) __bf16 pT[HB][kTile][kPRow];
     __shared__ __attribute__((aligned(16))) float alpha_s[HB * 32];
     __shared__ __attribute__((aligned(16))) float l_s[HB * 32];
     __shared__ __attribute__((aligned(16))) int flag_s[WAVES];
@@ -347,22 +353,27 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) alpha_s[hb * 32 + 8 * qq + 4 * half + ii] = 1.0f;
         }
+        i16x4 pw;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
             // A present entry has a finite reference max (its logit set
             // one if none was); an absent one gets 0.
             const float p = valid ? __builtin_amdgcn_exp2f(x[ii] - mref[ii]) : 0.0f;
             lsum[ii] += p;
-            pbuf[hb * 32 + 8 * qq + 4 * half + ii][col] = (__bf16)p;
+            pw[ii] = __builtin_bit_cast(short, (__bf16)p);
         }
+        *(i16x4 *)&pT[hb][col][8 * qq + 4 * half] = pw;
         if (lane == 0) flag_s[wave] = wave_need ? 1 : 0;
         lds_barrier();
         if (t + 1 < ntiles) write_parts();
         // 3. O = alpha * O + P V for head block hb, dims qq*DV/4 .. +DV/4-1.
         u32x4 fl;
-        bf16x8 pab[2];
-        lds_read_fp(&flag_s[hb * 4], &pbuf[hb * 32 + col][half * 8], &pbuf[hb * 32 + col][16 + half * 8], fl,
-                    pab[0], pab[1]);
+        i16x4 t00, t01, t10, t11;
+        lds_read_fp(&flag_s[hb * 4], &pT[hb][eb][dl], &pT[hb][eb + 4][dl], &pT[hb][16 + eb][dl],
+                    &pT[hb][16 + eb + 4][dl], fl, t00, t01, t10, t11);
+        const i16x8 pa0 = {t00[0], t00[1], t00[2], t00[3], t01[0], t01[1], t01[2], t01[3]};
+        const i16x8 pa1 = {t10[0], t10[1], t10[2], t10[3], t11[0], t11[1], t11[2], t11[3]};
+        const bf16x8 pab[2] = {__builtin_bit_cast(bf16x8, pa0), __builtin_bit_cast(bf16x8, pa1)};
         const bool resc = __builtin_amdgcn_readfirstlane((int)(fl[0] | fl[1] | fl[2] | fl[3])) != 0;  // block-uniform
         if (resc) {
 #pragma unroll

@@ -348,10 +348,6 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
                 }
                 if (col == 0) alpha_s[hb * 32 + 8 * qq + 4 * half + ii] = alpha;
             }
-        } else if (col == 0) {
-            // Another wave of the head block may rescale: these heads keep 1.
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) alpha_s[hb * 32 + 8 * qq + 4 * half + ii] = 1.0f;
         }
         i16x4 pw;
 #pragma unroll
@@ -378,7 +374,10 @@ __global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
         if (resc) {
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) {
-                const f32x4 al = *(const f32x4 *)&alpha_s[hb * 32 + 8 * j4 + 4 * half];
+                // A wave whose flag is clear wrote no factors this tile:
+                // its heads keep 1.
+                f32x4 al = *(const f32x4 *)&alpha_s[hb * 32 + 8 * j4 + 4 * half];
+                if (fl[j4] == 0u) al = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
                 for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll

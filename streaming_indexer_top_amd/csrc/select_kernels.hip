@@ -551,13 +551,12 @@ __device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_e
         const uint32_t incl = wave_incl_sum(cnt);
         const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
         if (tot == 0u) return;  // wave-uniform
-        uint32_t ba = 0, bb = 0;
-        if (lane == 0) {
-            if (tot & 0xFFFFu) ba = atomicAdd(&sh.nA, tot & 0xFFFFu);
-            if (tot >> 16) bb = atomicAdd(&sh.nB, tot >> 16);
-        }
-        ba = (uint32_t)__builtin_amdgcn_readfirstlane((int)ba);
-        bb = (uint32_t)__builtin_amdgcn_readfirstlane((int)bb);
+        // Lanes 0 and 1 reserve the wave's A and B slots with one LDS
+        // atomic instruction (adding 0 is harmless).
+        uint32_t bx = 0;
+        if (lane < 2) bx = atomicAdd(lane ? &sh.nB : &sh.nA, lane ? (tot >> 16) : (tot & 0xFFFFu));
+        const uint32_t ba = (uint32_t)__builtin_amdgcn_readlane((int)bx, 0);
+        const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)bx, 1);
         const uint32_t excl = incl - cnt;
         uint32_t pa = ba + (excl & 0xFFFFu);
         uint32_t pb = (uint32_t)kCapA + bb + (excl >> 16);

@@ -222,26 +222,6 @@ int csa_sparse_attention(const void *q, const void *kv, const int32_t *idx, void
                          int32_t dtype, int64_t S, int64_t T, int32_t H, int32_t D_K,
                          int32_t D_V, int64_t k, float scale, void *stream);
 
-/*
- * Register-only MFMA rate probe: a measurement aid, not a step of the
- * indexer or the attention.  Launches `blocks` workgroups of 256 threads;
- * every wave issues `iters` x 4 v_mfma_f32_32x32x16_bf16 (four independent
- * accumulation chains) on pseudo-random bf16 operands held in registers,
- * with no LDS or memory traffic but one float per thread stored to out at
- * the end.  rotate != 0 cycles each MFMA through four operand fragments per
- * side (inputs change on every issue); rotate == 0 keeps one pair.  Flops
- * per launch: blocks * 4 waves * iters * 4 * 32768.  Timing it against the
- * nominal bf16 peak gives the rate the matrix pipe sustains under its own
- * power draw.
- *
- *   out  [blocks * 256]  float (4-byte aligned), overwritten
- *
- * blocks in [1, 2^20] and iters in [4, 2^24], a multiple of 4, else
- * CSA_ERR_BAD_SHAPE; out NULL gives CSA_ERR_NULL_PTR.  Enqueued on
- * `stream`; allocates nothing.
- */
-int csa_probe_mfma(float *out, int32_t blocks, int32_t iters, int32_t rotate, void *stream);
-
 #ifdef __cplusplus
 }
 #endif

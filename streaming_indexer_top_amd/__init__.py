@@ -8,5 +8,5 @@ over its selected entries.  ``inputs`` holds the seeded synthetic input
 generators.
 """
 from .binding import (CsaError, abi_version, library_path, load_library,  # noqa: F401
-                      probe_mfma, profile_collect, profile_enable, sparse_attention, topk,
+                      profile_collect, profile_enable, sparse_attention, topk,
                       workspace_size)

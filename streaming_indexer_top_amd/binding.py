@@ -27,7 +27,7 @@ KERNEL_NAMES = ("score", "select", "merge", "attention")
 
 EXPORTS = ("csa_abi_version", "csa_status_str", "csa_indexer_topk_workspace_size",
            "csa_indexer_topk", "csa_indexer_topk_batched", "csa_profile_enable",
-           "csa_profile_collect", "csa_sparse_attention", "csa_probe_mfma")
+           "csa_profile_collect", "csa_sparse_attention")
 
 
 class CsaError(RuntimeError):
@@ -86,8 +86,6 @@ def load_library(path: str | None = None):
     lib.csa_sparse_attention.argtypes = [vp, vp, vp, vp, i32, i64, i64, i32, i32, i32, i64,
                                          ctypes.c_float, vp]
     lib.csa_sparse_attention.restype = ctypes.c_int
-    lib.csa_probe_mfma.argtypes = [vp, i32, i32, i32, vp]
-    lib.csa_probe_mfma.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -250,22 +248,6 @@ def sparse_attention(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, d_v: 
             ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(kv.data_ptr()),
             ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(out.data_ptr()), CSA_BF16,
             S, T, H, DK, int(d_v), k, float(scale), ctypes.c_void_p(stream)))
-    return out
-
-
-def probe_mfma(blocks: int, iters: int, rotate: bool = True, out: torch.Tensor | None = None):
-    """Register-only MFMA rate probe (a measurement aid): enqueues blocks x
-    256 threads of bf16 32x32x16 MFMA chains on torch's current stream and
-    returns the [blocks * 256] float sink.  Flops: blocks * 4 * iters * 4 *
-    32768."""
-    if not torch.cuda.is_available():
-        raise RuntimeError("probe_mfma needs a GPU")
-    dev = torch.device("cuda", torch.cuda.current_device())
-    if out is None:
-        out = torch.empty((blocks * 256,), dtype=torch.float32, device=dev)
-    lib = load_library()
-    _check(lib.csa_probe_mfma(ctypes.c_void_p(out.data_ptr()), int(blocks), int(iters), 1 if rotate else 0,
-                              ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)))
     return out
 
 

@@ -12,8 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa_indexer.so")
-SOURCES = ["csa_api.hip", "score_kernels.hip", "select_kernels.hip", "attention_kernels.hip",
-           "probe_kernels.hip"]
+SOURCES = ["csa_api.hip", "score_kernels.hip", "select_kernels.hip", "attention_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -55,12 +55,31 @@ def gaussian_fp32(S: int, T: int, H: int, D: int, seed: int, device="cpu"):
     return q, w, kc
 
 
+def _randint_sliced(lo, hi, shape, g, device, out_dtype):
+    """Uniform integers on [lo, hi) drawn row-slice by row-slice (the int64
+    draws of a whole large tensor would need 4x its bf16 size), stored as
+    ``out_dtype``."""
+    out = torch.empty(shape, dtype=out_dtype, device=device)
+    if out.numel() == 0:
+        return out
+    row_elems = max(1, out[0].numel())
+    step = max(1, _SLICE_ELEMS // row_elems)
+    for r0 in range(0, shape[0], step):
+        r1 = min(shape[0], r0 + step)
+        out[r0:r1].copy_(torch.randint(lo, hi, (r1 - r0, *shape[1:]), generator=g, device=device))
+    return out
+
+
 def integer_valued(S: int, T: int, H: int, D: int, seed: int, dtype=torch.float32,
                    signed_w: bool = False, device="cpu"):
     """Integer-valued inputs, exact in fp32 and bf16: q, kc uniform on
-    {-3..3}; w uniform on {1, 2}, or on {-2, -1, 1, 2} when ``signed_w``."""
+    {-3..3}; w uniform on {1, 2}, or on {-2, -1, 1, 2} when ``signed_w``.
+    A q of more than 2^28 elements is drawn in row slices."""
     g = _gen(seed, device)
-    q = torch.randint(-3, 4, (S, H, D), generator=g, device=device).to(dtype)
+    if S * H * D > _SLICE_ELEMS:
+        q = _randint_sliced(-3, 4, (S, H, D), g, device, dtype)
+    else:
+        q = torch.randint(-3, 4, (S, H, D), generator=g, device=device).to(dtype)
     if signed_w:
         wi = torch.randint(0, 4, (S, H), generator=g, device=device)
         table = torch.tensor([-2, -1, 1, 2], device=device)

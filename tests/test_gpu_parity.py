@@ -543,13 +543,34 @@ def test_cfg5_sampled():
     _full_shape_check(5, sample=256, shard_tail=8192)
 
 
-def test_mfma_probe_runs_and_is_deterministic():
-    """The register-only MFMA probe (a measurement aid) runs through the C
-    ABI, writes one finite float per thread, and repeats bit for bit."""
-    a = csa.probe_mfma(8, 16, rotate=True)
-    b = csa.probe_mfma(8, 16, rotate=True)
-    c = csa.probe_mfma(8, 16, rotate=False)
-    torch.cuda.synchronize()
-    assert a.shape == (8 * 256,)
-    assert torch.isfinite(a).all() and torch.isfinite(c).all()
-    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+@pytest.mark.slow
+def test_cfg5_integer_sampled():
+    """The long-context shape (S = 2^20, T = 262,144) with signed integer
+    inputs through the default plan (four 65,536-key chunks per long row,
+    running lists merged after every chunk, many passes): 256 sampled rows,
+    boundary rows included, bit for bit against the oracle.  Integer scores
+    tie densely (about 15 keys share each value near the k-th), so the
+    (score desc, index asc) order is exercised across chunk boundaries."""
+    _full_shape_check(5, sample=256, integer=True)
+
+
+def test_full_size_chunk_and_tile_grid_integer_bit_exact():
+    """Rows that see all 262,144 keys of the long-context key table, signed
+    integer inputs: every chunk size of the page's sweep (4,096 .. 65,536
+    keys, i.e. 64 .. 4 chunks merged into the running lists) times every key
+    tile (64, 128, 256), plus the automatic plan (key splits) and forced
+    split counts, equals the oracle bit for bit."""
+    S, T, H, D, m, k = 128, 262144, 64, 128, 4, 2048
+    q_pos0 = m * T - S  # rows see T-31 .. T keys
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=90, dtype=torch.bfloat16, signed_w=True)
+    say("full-size chunk/tile grid S=%d T=%d k=%d q_pos0=%d" % (S, T, k, q_pos0))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    qd, wd, kd = q.to(DEV), w.to(DEV), kc.to(DEV)
+    settings = [dict(chunk_keys=c, key_tile=t) for c in (4096, 8192, 16384, 32768, 65536)
+                for t in (64, 128, 256)]
+    settings += [dict(), dict(key_splits=1), dict(key_splits=4), dict(key_splits=64)]
+    for kw in settings:
+        say("  %s" % kw)
+        idx, sc = csa.topk(qd, wd, kd, m, k, q_pos0=q_pos0, **kw)
+        torch.cuda.synchronize()
+        assert_no_fail(checks.check_exact(idx.cpu().numpy(), sc.cpu().numpy(), o_idx, o_sc))

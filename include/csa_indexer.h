@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 /* Status codes. */
 #define CSA_OK 0
@@ -68,6 +68,8 @@ extern "C" {
 #define CSA_ERR_UNSUPPORTED 6         /* valid request outside what this build implements */
 #define CSA_ERR_HIP 7                 /* a HIP call or kernel launch failed */
 #define CSA_ERR_BAD_OPTION 8          /* a field of csa_opts is out of range */
+#define CSA_ERR_SCRATCH_TOO_SMALL 9   /* allocation-free call: one query block needs more
+                                         than CSA_NOALLOC_SCRATCH_BYTES */
 
 /* Input dtypes (q, w and kc share one). */
 #define CSA_F32 0  /* IEEE fp32 */
@@ -146,6 +148,37 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
                      int64_t k, int64_t q_pos0, int32_t *idx, float *score,
                      void *workspace, size_t workspace_bytes, const csa_opts *opts,
                      void *stream);
+
+/*
+ * Allocation-free form of csa_indexer_topk, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same operation, arguments, layouts, options,
+ * outputs and kernels, but no workspace argument.  Its scratch is a fixed
+ * device array of CSA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's first use on that GPU until the process ends.
+ * The call plans its passes for that size (opts->workspace_budget, if set,
+ * can only lower it), so the outputs are bit-identical to csa_indexer_topk's
+ * for the same inputs; with large problems it takes more passes.
+ *
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams, or from different host threads without an
+ * order between them) race and give undefined results.  Calls ordered on
+ * one stream are fine.  Nothing in the scratch needs to start at zero; its
+ * contents after a call are unspecified.
+ *
+ * Errors as for csa_indexer_topk, plus CSA_ERR_SCRATCH_TOO_SMALL when one
+ * query block's share (8 rows x (4 x chunk keys + list and summary bytes))
+ * exceeds the scratch, e.g. with a caller-fixed chunk_keys of 2^23 or more
+ * keys.  Argument checks, that one included, run before any HIP call.  On its
+ * first call on a GPU it looks up the scratch address there (no allocation);
+ * a failed lookup gives CSA_ERR_HIP.  It allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int csa_indexer_topk_noalloc(const void *q, const void *w, const void *kc, int32_t dtype,
+                             int64_t S, int64_t T, int32_t H_I, int32_t D_I, int32_t m,
+                             int64_t k, int64_t q_pos0, int32_t *idx, float *score,
+                             const csa_opts *opts, void *stream);
 
 /*
  * Batched form (B=1 is the single call above): B independent problems of the

@@ -9,4 +9,4 @@ generators.
 """
 from .binding import (CsaError, abi_version, library_path, load_library,  # noqa: F401
                       profile_collect, profile_enable, sparse_attention, topk,
-                      workspace_size)
+                      topk_noalloc, workspace_size)

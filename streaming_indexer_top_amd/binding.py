@@ -27,7 +27,7 @@ KERNEL_NAMES = ("score", "select", "merge", "attention")
 
 EXPORTS = ("csa_abi_version", "csa_status_str", "csa_indexer_topk_workspace_size",
            "csa_indexer_topk", "csa_indexer_topk_batched", "csa_profile_enable",
-           "csa_profile_collect", "csa_sparse_attention")
+           "csa_profile_collect", "csa_sparse_attention", "csa_indexer_topk_noalloc")
 
 
 class CsaError(RuntimeError):
@@ -78,6 +78,9 @@ def load_library(path: str | None = None):
                                              i64, vp, vp, vp, ctypes.c_size_t,
                                              ctypes.POINTER(csa_opts), vp]
     lib.csa_indexer_topk_batched.restype = ctypes.c_int
+    lib.csa_indexer_topk_noalloc.argtypes = [vp, vp, vp, i32, i64, i64, i32, i32, i32, i64, i64,
+                                             vp, vp, ctypes.POINTER(csa_opts), vp]
+    lib.csa_indexer_topk_noalloc.restype = ctypes.c_int
     lib.csa_profile_enable.argtypes = [ctypes.c_int]
     lib.csa_profile_enable.restype = ctypes.c_int
     lib.csa_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double),
@@ -205,6 +208,50 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
                 ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(score.data_ptr()),
                 ctypes.c_void_p(workspace.data_ptr()), nbytes, ctypes.byref(o),
                 ctypes.c_void_p(stream)))
+    return idx, score
+
+
+def topk_noalloc(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
+                 q_pos0: int = 0, chunk_keys: int = 0, key_tile: int = 0,
+                 workspace_budget: int = 0, key_splits: int = 0, out: tuple | None = None):
+    """``topk`` through the library's allocation-free entry point: no
+    workspace (the library's fixed per-GPU scratch serves instead).  Pass
+    ``out`` = (idx, score) to allocate nothing at all.  Calls that overlap
+    on one GPU share that scratch and race; calls ordered on one stream do
+    not."""
+    if q.dim() != 3 or w.dim() != 2 or kc.dim() != 2:
+        raise ValueError("q must be [S,H,D], w [S,H], kc [T,D]")
+    S, H, D = q.shape
+    T = kc.shape[0]
+    if tuple(w.shape) != (S, H) or kc.shape[1] != D:
+        raise ValueError("shape mismatch: q %s, w %s, kc %s"
+                         % (tuple(q.shape), tuple(w.shape), tuple(kc.shape)))
+    if not (q.dtype == w.dtype == kc.dtype):
+        raise TypeError("q, w, kc must share one dtype")
+    dev = q.device
+    if dev.type != "cuda" or w.device != dev or kc.device != dev:
+        raise ValueError("q, w, kc must be on one GPU device")
+    for name, t in (("q", q), ("w", w), ("kc", kc)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if out is None:
+        idx = torch.empty((S, k), dtype=torch.int32, device=dev)
+        score = torch.empty((S, k), dtype=torch.float32, device=dev)
+    else:
+        idx, score = out
+        if tuple(idx.shape) != (S, k) or tuple(score.shape) != (S, k) \
+                or idx.dtype != torch.int32 or score.dtype != torch.float32 \
+                or not idx.is_contiguous() or not score.is_contiguous():
+            raise ValueError("out must be contiguous int32/float32 tensors of shape %s"
+                             % ((S, k),))
+    o = _opts(chunk_keys, key_tile, workspace_budget, key_splits)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        _check(load_library().csa_indexer_topk_noalloc(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(w.data_ptr()),
+            ctypes.c_void_p(kc.data_ptr()), _dtype_code(q.dtype), S, T, H, D, int(m), int(k),
+            int(q_pos0), ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(score.data_ptr()),
+            ctypes.byref(o), ctypes.c_void_p(stream)))
     return idx, score
 
 

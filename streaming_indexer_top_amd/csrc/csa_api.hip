@@ -24,6 +24,12 @@
 
 #include "csa_internal.h"
 
+// Scratch of the allocation-free entry point: one fixed array per GPU, held
+// from the library's first use there until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: the device
+// address comes from hipGetSymbolAddress, once per device (scratch_on).
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int64_t kDefaultBudget = int64_t(2) << 30;
@@ -41,6 +47,29 @@ constexpr int64_t kSplitMinKeys = 2048;
 constexpr int32_t kMaxSplits = 64;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+static_assert(CSA_NOALLOC_SCRATCH_BYTES % kAlign == 0, "scratch size in whole alignment units");
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_ptr;  // by device ordinal; null until looked up
+
+// Device address of the current device's scratch (looked up on first use).
+int scratch_on(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CSA_ERR_HIP;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return CSA_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA_OK;
+}
 
 struct Plan {
     int64_t n_max = 0;   // keys usable by the last row
@@ -227,6 +256,7 @@ const char *csa_status_str(int status)
     case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 4096 or T >= 2^31)";
     case CSA_ERR_HIP: return "HIP call or kernel launch failed";
     case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256 up to 2^24, key_tile one of 64/128/256, key_splits 0 or a power of two up to 64, reserved fields 0";
+    case CSA_ERR_SCRATCH_TOO_SMALL: return "allocation-free call: one query block needs more scratch than the library's fixed 256 MiB (use a smaller chunk_keys, or csa_indexer_topk with a workspace)";
     default: return "unknown status";
     }
 }
@@ -419,6 +449,34 @@ int csa_indexer_topk(const void *q, const void *w, const void *kc, int32_t dtype
                               workspace, workspace_bytes, opts, &p, &rows);
     if (st != CSA_OK) return st;
     return run_call(q, w, kc, dtype, S, T, H_I, D_I, m, k, q_pos0, idx, score, workspace, p, rows,
+                    stream);
+}
+
+int csa_indexer_topk_noalloc(const void *q, const void *w, const void *kc, int32_t dtype,
+                             int64_t S, int64_t T, int32_t H_I, int32_t D_I, int32_t m,
+                             int64_t k, int64_t q_pos0, int32_t *idx, float *score,
+                             const csa_opts *opts, void *stream)
+{
+    // The plan is made for the scratch size: a caller's budget can only
+    // lower it.  The checks run on a stand-in workspace pointer (aligned,
+    // never dereferenced) so that none of them needs a HIP call.
+    csa_opts o{};
+    if (opts) o = *opts;
+    const int64_t cap = (int64_t)CSA_NOALLOC_SCRATCH_BYTES;
+    if (o.workspace_budget >= 0 && (o.workspace_budget == 0 || o.workspace_budget > cap))
+        o.workspace_budget = cap;
+    Plan p;
+    int64_t rows = 0;
+    int st = check_call(q, w, kc, dtype, S, T, H_I, D_I, m, k, q_pos0, idx, score,
+                        (void *)kAlign, CSA_NOALLOC_SCRATCH_BYTES, &o, &p, &rows);
+    if (st == CSA_ERR_WORKSPACE_TOO_SMALL) return CSA_ERR_SCRATCH_TOO_SMALL;
+    if (st != CSA_OK) return st;
+    void *ws = nullptr;
+    if (S > 0 && p.chunk > 0) {
+        st = scratch_on(&ws);
+        if (st != CSA_OK) return st;
+    }
+    return run_call(q, w, kc, dtype, S, T, H_I, D_I, m, k, q_pos0, idx, score, ws, p, rows,
                     stream);
 }
 

@@ -35,8 +35,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     lib = csa.load_library()
-    assert lib.csa_abi_version() == 3
-    for st in range(0, 10):
+    assert lib.csa_abi_version() == 4
+    for st in range(0, 11):
         assert lib.csa_status_str(st)
 
 
@@ -207,3 +207,35 @@ def test_sparse_attention_null_and_alignment_checks():
     # No rows: nothing to do, nothing touched.
     assert lib.csa_sparse_attention(z, z, z, z, binding.CSA_BF16, 0, 10, 64, 576, 512, 8,
                                     0.1, None) == 0
+
+
+def test_noalloc_rejects_beyond_scratch_before_any_hip_call():
+    """The allocation-free entry point checks everything before any HIP call
+    (dummy device pointers: nothing is dereferenced).  One query block of 8
+    rows against a caller-fixed 2^24-key chunk needs 512 MiB of scores, above
+    the 256 MiB scratch: CSA_ERR_SCRATCH_TOO_SMALL.  Bad arguments give the
+    same codes as csa_indexer_topk."""
+    lib = csa.load_library()
+    p = ctypes.c_void_p(256)
+    T = 1 << 24
+    big = binding._opts(chunk_keys=1 << 24)
+    assert lib.csa_indexer_topk_noalloc(p, p, p, binding.CSA_BF16, 8, T, 64, 128, 1, 16, T,
+                                        p, p, ctypes.byref(big), None) == 9
+    assert b"256 MiB" in lib.csa_status_str(9)
+    # Same shapes with a chunk that fits: no error before the HIP part, so
+    # only argument errors are probed here.
+    assert lib.csa_indexer_topk_noalloc(p, p, p, 7, 8, 100, 64, 128, 1, 16, 0, p, p, None,
+                                        None) == 3
+    assert lib.csa_indexer_topk_noalloc(p, p, p, 1, 8, 100, 64, 128, 0, 16, 0, p, p, None,
+                                        None) == 2
+    assert lib.csa_indexer_topk_noalloc(ctypes.c_void_p(0), p, p, 1, 8, 100, 64, 128, 1, 16, 0,
+                                        p, p, None, None) == 1
+    assert lib.csa_indexer_topk_noalloc(p, p, p, 1, 8, 100, 64, 128, 1, 5000, 0, p, p, None,
+                                        None) == 6
+    neg = binding._opts(workspace_budget=-1)
+    assert lib.csa_indexer_topk_noalloc(p, p, p, 1, 8, 100, 64, 128, 1, 16, 0, p, p,
+                                        ctypes.byref(neg), None) == 8
+    # No rows: nothing to do, no scratch needed, nothing touched.
+    z = ctypes.c_void_p(0)
+    assert lib.csa_indexer_topk_noalloc(z, z, z, 1, 0, 100, 64, 128, 1, 16, 0, z, z, None,
+                                        None) == 0

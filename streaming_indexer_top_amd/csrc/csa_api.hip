@@ -82,7 +82,7 @@ struct Plan {
 };
 
 // Workspace layout of a pass of `rows` rows, in this order:
-//   scores [rows][chunk] fp32 | meta [splits*rows] ChunkMeta |
+//   scores [rows][chunk] u32 (orderable fp32) | meta [splits*rows] ChunkMeta |
 //   (several chunks or splits:) lists [splits*rows][k] u64 | state [splits*rows] RowState
 struct PassLayout {
     size_t meta, lists, state, end;
@@ -93,7 +93,7 @@ PassLayout pass_layout(const Plan &p, int64_t rows, int64_t k)
     PassLayout l{0, 0, 0, 0};
     if (p.chunk == 0 || rows <= 0) return l;
     const size_t vrows = (size_t)rows * (size_t)p.splits;
-    l.meta = align_up((size_t)rows * (size_t)p.chunk * sizeof(float));
+    l.meta = align_up((size_t)rows * (size_t)p.chunk * sizeof(uint32_t));
     l.end = l.meta + align_up(vrows * sizeof(csa::ChunkMeta));
     if (p.lists) {
         l.lists = l.end;
@@ -357,7 +357,7 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
         const int64_t n_hi = csa::n_usable(q_pos0 + r0 + nr - 1, T, m);
         const int64_t nch = (p.chunk > 0 && n_hi > 0) ? (n_hi + p.chunk - 1) / p.chunk : 1;
         const PassLayout lay = pass_layout(p, nr, k);
-        float *ws_scores = (float *)wsb;
+        uint32_t *ws_scores = (uint32_t *)wsb;
         csa::ChunkMeta *meta = p.chunk > 0 ? (csa::ChunkMeta *)(wsb + lay.meta) : nullptr;
         uint64_t *lists = p.lists ? (uint64_t *)(wsb + lay.lists) : nullptr;
         csa::RowState *state = p.lists ? (csa::RowState *)(wsb + lay.state) : nullptr;

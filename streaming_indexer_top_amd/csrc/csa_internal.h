@@ -51,7 +51,7 @@ struct ScoreArgs {
     const void *q;    // [S][H][D], rows of this batch start at row0
     const void *w;    // [S][H]
     const void *kc;   // [T][D]
-    float *ws;        // [rows][clen] head-reduced scores of this chunk
+    uint32_t *ws;     // [rows][clen] head-reduced scores of this chunk, as orderable()
     ChunkMeta *meta;  // [rows] chunk summary (bf16 path only; may be null)
     const RowState *state;  // [rows] theta from earlier chunks, or null
     int64_t k;
@@ -73,7 +73,7 @@ struct ScoreArgs {
 // leaves its sorted best k in lists / state at that index (first = 1,
 // emit = 0); the merge kernel then combines the splits' lists.
 struct SelectArgs {
-    const float *ws;      // [rows][clen] scores written by the score pass
+    const uint32_t *ws;   // [rows][clen] orderable() scores written by the score pass
     const ChunkMeta *meta;  // [nsplit*rows] chunk summaries, or null (then no shortcut)
     uint64_t *lists;      // [nsplit*rows][k] running best-k lists, sorted descending
     RowState *state;      // [nsplit*rows] running list length and k-th key

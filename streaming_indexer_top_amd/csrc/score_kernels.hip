@@ -7,9 +7,11 @@
 //
 //     s(i,j) = sum_h w[i,h] * max(q[i,h,:] . kc[j,:], 0)
 //
-// and the result for the chunk goes to a workspace slice [rows][clen].  Only
-// the head-reduced score leaves the kernel; the per-head logits live in
-// registers, so the [S,H_I,T] tensor never exists.
+// and the result for the chunk goes to a workspace slice [rows][clen], each
+// score stored as its orderable() integer (the monotone fp32 -> u32 map that
+// the selection compares).  Only the head-reduced score leaves the kernel;
+// the per-head logits live in registers, so the [S,H_I,T] tensor never
+// exists.
 //
 // bf16 path: the contraction over the head dimension is a dense GEMM
 // [H_I, D_I] x [D_I, N] per query, run on the MFMA units with
@@ -36,12 +38,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ inline float bf16_bits_to_float(uint16_t b)
 {
     return __uint_as_float(((uint32_t)b) << 16);
-}
-
-// Inverse of orderable(): the fp32 score of an orderable key.
-__device__ inline float key_score_of(uint32_t u)
-{
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
 // Buffer resource of `bytes` bytes at `base` (raw, stride 0); accesses at
@@ -280,10 +276,9 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
 
     // Scores are stored and counted 64 keys at a time (2 blocks): chunk-
     // relative 32-bit key offsets, one lane per key.
-    float *wsrow = a.ws + (active ? rl : 0) * a.clen + split * a.slen;
+    uint32_t *wsrow = a.ws + (active ? rl : 0) * a.clen + split * a.slen;
     const __amdgpu_buffer_rsrc_t ws_rs = buffer_rsrc(wsrow, (uint32_t)((kcap - kb0) * 4));
     const int my_len = (int)(my_end - kb0);  // keys of this row in the chunk
-    const float f_floor = filt ? key_score_of(u_floor) : 0.0f;
     uint32_t *h = hist_all + wave * kHistBins;
 
     // Per-lane share of one block, over register half rh (8 of the 16
@@ -309,14 +304,15 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
         const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe), __float_as_uint(po),
                                                         false, false);
         const float sc = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+        const uint32_t u = orderable_nz(sc);
         const int rel = rel0 + lane;
         const bool valid = real && rel < my_len;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), ws_rs, lane * 4, rel0 * 4, 0);
-        const uint32_t inc = (valid && (!filt || sc > f_floor)) ? 1u : 0u;
+        __builtin_amdgcn_raw_buffer_store_b32(u, ws_rs, lane * 4, rel0 * 4, 0);
+        const uint32_t inc = (valid && (!filt || u > u_floor)) ? 1u : 0u;
         // A plain LDS atomic here would make the compiler wait for every
         // tile DMA in flight; the add does not touch the tiles.
         const uint32_t hp = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint32_t *)(
-            h + (orderable_nz(sc) >> (32 - kHistBits)));
+            h + (u >> (32 - kHistBits)));
         asm volatile("ds_add_u32 %0, %1" ::"v"(hp), "v"(inc));
     };
 
@@ -501,7 +497,7 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a)
         for (int d = 0; d < D; ++d) acc = fmaf(qs[h * D + d], kr[d], acc);
         s = fmaf(wsh[h], fmaxf(acc, 0.0f), s);
     }
-    a.ws[rl * a.clen + (gk - a.c0)] = s;
+    a.ws[rl * a.clen + (gk - a.c0)] = orderable(s);
 }
 
 template <int D, int HT, int NT, bool DB, int WAVES>

@@ -25,6 +25,8 @@
 // ones to two LDS regions.  One bucket sort over both regions orders them;
 // the first k are the chunk's best k.  The workgroup needs about 39 KB of LDS,
 // so four rows share a CU.
+#include <type_traits>
+
 #include "csa_internal.h"
 
 namespace csa {
@@ -65,11 +67,6 @@ __device__ inline int32_t key_index(uint64_t key)
 __device__ inline float score_of_orderable(uint32_t u)
 {
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-
-__device__ inline uint64_t make_key(float sc, uint32_t j)
-{
-    return ((uint64_t)orderable(sc) << 32) | (uint64_t)(0xFFFFFFFFu - j);
 }
 
 __device__ inline uint32_t lanes_below(uint64_t mask)
@@ -477,24 +474,24 @@ __device__ __forceinline__ void sort_keys(uint64_t *cand, int nA, int nB, uint32
 
 // Row context shared by the selection strategies below.
 struct RowCtx {
-    const float *src;  // the row's chunk scores (a workspace row of clen floats)
-    int64_t len;       // keys of this row in the chunk
-    uint32_t c0;       // first key index of the chunk
-    bool filt;         // keys must beat f_floor (the running list is full)
-    float f_floor;
+    const uint32_t *src;  // the row's chunk scores as orderable() (a workspace row of clen)
+    int64_t len;          // keys of this row in the chunk
+    uint32_t c0;          // first key index of the chunk
+    uint32_t u_lo;        // keys below this orderable score cannot enter the running best k
+                          // (the list's k-th score + 1 when the list is full, else 0)
 };
 
-// Loads 16 consecutive scores of a workspace row at `base`; at or past len
-// it loads the row's first 16 instead (callers ignore positions >= len).
-// Unconditional, so that the compiler can count the loads in flight and wait
-// only for the ones it needs.  Stays inside the row: base is a multiple of
-// 16 below len <= row length, which is a multiple of 256.
-__device__ inline void load16(const float *src, int64_t len, int64_t base, float (&v)[16])
+// Loads 16 consecutive orderable scores of a workspace row at `base`; at or
+// past len it loads the row's first 16 instead (callers ignore positions >=
+// len).  Unconditional, so that the compiler can count the loads in flight
+// and wait only for the ones it needs.  Stays inside the row: base is a
+// multiple of 16 below len <= row length, which is a multiple of 256.
+__device__ inline void load16(const uint32_t *src, int64_t len, int64_t base, uint32_t (&v)[16])
 {
-    const float *p = src + (base < len ? base : 0);
+    const uint32_t *p = src + (base < len ? base : 0);
 #pragma unroll
     for (int i = 0; i < 16; i += 4) {
-        const float4 x = *(const float4 *)(p + i);
+        const uint4 x = *(const uint4 *)(p + i);
         v[i] = x.x;
         v[i + 1] = x.y;
         v[i + 2] = x.z;
@@ -504,15 +501,15 @@ __device__ inline void load16(const float *src, int64_t len, int64_t base, float
 
 // One streaming pass over the row's chunk scores, 16 consecutive keys per
 // thread per round, the next two rounds' loads in flight while this round is
-// classified.  A key beating the floor goes to region A (cand[0..)) if its
-// score is >= f_sure, to region B (cand[A..)) if it is >= f_edge, else it
-// is dropped.  Each wave reserves its slots with one LDS atomic per region
-// per round; the order inside a region is arbitrary (the sort fixes it).
-// Returns the region sizes (clamped to the capacities, which the callers'
-// counts never exceed).
+// classified.  With eA >= eB >= r.u_lo: a key whose orderable score u has
+// u >= eA goes to region A (cand[0..)), one with eB <= u < eA to region B
+// (cand[A..)), any other is dropped.  Each wave reserves its slots with one
+// LDS atomic per region per round; the order inside a region is arbitrary
+// (the sort fixes it).  Returns the region sizes (clamped to the capacities,
+// which the callers' counts never exceed).
 template <int K>
-__device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_edge, uint64_t *cand,
-                        SelectShared &sh, int tid, int &nA, int &nB)
+__device__ __forceinline__ void collect(const RowCtx &r, uint32_t eA, uint32_t eB, uint64_t *cand,
+                                        SelectShared &sh, int tid, int &nA, int &nB)
 {
     constexpr int kCapA = Caps<K>::A;
     constexpr int kCapB = Caps<K>::B;
@@ -524,30 +521,24 @@ __device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_e
         sh.nB = 0u;
     }
     __syncthreads();
-    // Without a floor every key in range is eligible (also -inf and NaN, which
-    // then fail both thresholds or pass f_edge = -inf exactly as compared).
-    const bool nofilt = !r.filt;
     // Each lane's slot for the keys it drops: the bucket words behind the
     // candidate regions are unused until the sort, and one slot per lane keeps
     // the stores of a wave free of same-address conflicts.
     const uint32_t dummy = (uint32_t)Caps<K>::Cand + (uint32_t)tid;
-    auto process = [&](const float (&v)[V], int64_t base) {
-        // Classification without branches: 2 bits per key (1 = region A,
-        // 2 = region B, 0 = dropped) and the two counts packed in one word.
-        const int64_t rem64 = r.len - base;
-        const int rem = rem64 <= 0 ? 0 : (rem64 >= V ? V : (int)rem64);
-        uint32_t cls = 0, cnt = 0;
+    // FULL: every lane's 16 keys lie inside the row (all rounds but the
+    // row's last), so no key needs a range test.
+    auto process = [&](const uint32_t (&v)[V], int64_t base, auto full_t) {
+        constexpr bool FULL = decltype(full_t)::value;
+        const int rem = FULL ? V : (int)min((int64_t)V, max((int64_t)0, r.len - base));
+        // Counts: keys >= eA (A) and keys >= eB (A and B), no branches.
+        uint32_t ca = 0, cb = 0;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            const float x = v[i];
-            const bool ok = (i < rem) & (nofilt | (x > r.f_floor));
-            const bool ge_s = x >= f_sure;
-            const bool isA = ok & ge_s;
-            const bool isB = ok & !ge_s & (x >= f_edge);
-            cls |= (isA ? 1u : 0u) << (2 * i);
-            cls |= (isB ? 2u : 0u) << (2 * i);
-            cnt += (isA ? 1u : 0u) + (isB ? 0x10000u : 0u);
+            const bool in = FULL || i < rem;
+            ca += (in && v[i] >= eA) ? 1u : 0u;
+            cb += (in && v[i] >= eB) ? 1u : 0u;
         }
+        const uint32_t cnt = ca | ((cb - ca) << 16);  // A low, B high
         const uint32_t incl = wave_incl_sum(cnt);
         const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
         if (tot == 0u) return;  // wave-uniform
@@ -566,70 +557,77 @@ __device__ __forceinline__ void collect(const RowCtx &r, float f_sure, float f_e
                           bb + (tot >> 16) <= (uint32_t)kCapB;  // wave-uniform
         const uint32_t capA = fits ? 0xFFFFFFFFu : (uint32_t)kCapA;
         const uint32_t capB = fits ? 0xFFFFFFFFu : (uint32_t)(kCapA + kCapB);
-        // Every key is stored, a dropped one to this lane's spare slot.
-        const uint32_t j0 = r.c0 + (uint32_t)base;
+        // Every key is stored, a dropped one to this lane's spare slot.  The
+        // low word of a key is 0xFFFFFFFF - j, j = c0 + base + i.
+        const uint32_t nj0 = 0xFFFFFFFFu - (r.c0 + (uint32_t)base);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            const uint32_t c = (cls >> (2 * i)) & 3u;
-            const bool isA = c == 1u, isB = c == 2u;
-            const uint32_t slot = (isA & (pa < capA)) ? pa : ((isB & (pb < capB)) ? pb : dummy);
+            const bool in = FULL || i < rem;
+            const bool isA = in && v[i] >= eA;
+            const bool isAB = in && v[i] >= eB;
+            const uint32_t slot = (isA & (pa < capA)) ? pa : ((isAB & !isA & (pb < capB)) ? pb : dummy);
             pa += isA ? 1u : 0u;
-            pb += isB ? 1u : 0u;
-            cand[slot] = make_key(v[i], j0 + (uint32_t)i);
+            pb += (isAB & !isA) ? 1u : 0u;
+            cand[slot] = ((uint64_t)v[i] << 32) | (uint64_t)(nj0 - (uint32_t)i);
         }
     };
     // Three buffers rotate by name (the loop is unrolled by three): a copy
     // between buffers would wait for the load just issued into the source.
-    float b0[V], b1[V], b2[V];
+    uint32_t b0[V], b1[V], b2[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) b0[i] = b1[i] = b2[i] = 0.0f;
+    for (int i = 0; i < V; ++i) b0[i] = b1[i] = b2[i] = 0u;
     const int64_t lane0 = (int64_t)tid * V;
+    // Round starting at key rs: full rounds skip the range tests (uniform).
+    auto round = [&](const uint32_t (&v)[V], int64_t rs) {
+        if (rs + ROUND <= r.len) process(v, rs + lane0, std::true_type{});
+        else process(v, rs + lane0, std::false_type{});
+    };
     load16(r.src, r.len, lane0, b0);
     load16(r.src, r.len, ROUND + lane0, b1);
     for (int64_t e0 = 0; e0 < r.len; e0 += 3 * ROUND) {
         load16(r.src, r.len, e0 + 2 * ROUND + lane0, b2);
-        process(b0, e0 + lane0);
+        round(b0, e0);
         if (e0 + ROUND >= r.len) break;  // uniform
         load16(r.src, r.len, e0 + 3 * ROUND + lane0, b0);
-        process(b1, e0 + ROUND + lane0);
+        round(b1, e0 + ROUND);
         if (e0 + 2 * ROUND >= r.len) break;
         load16(r.src, r.len, e0 + 4 * ROUND + lane0, b1);
-        process(b2, e0 + 2 * ROUND + lane0);
+        round(b2, e0 + 2 * ROUND);
     }
     __syncthreads();
-    nA = (int)min(sh.nA, (uint32_t)kCapA);
-    nB = (int)min(sh.nB, (uint32_t)kCapB);
+    nA = __builtin_amdgcn_readfirstlane((int)min(sh.nA, (uint32_t)kCapA));
+    nB = __builtin_amdgcn_readfirstlane((int)min(sh.nB, (uint32_t)kCapB));
     __syncthreads();
 }
 
-// Splits the boundary bin [lo_u, hi_u) (orderable values, width 2^shift)
-// by its next 8 bits: a histogram over the chunk keys in the bin that beat
-// the floor gives the sub-bin holding the need-th best of them.  Narrows
-// [lo_u, hi_u) to it and returns the keys above it inside the old bin.
-__device__ __forceinline__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, uint32_t &hi_u, int shift,
-                               uint32_t need, uint32_t *hist, SelectShared &sh, int tid)
+// Splits the boundary bin [lo_u, hi_u) (orderable values, width 2^shift;
+// hi_u == 0: the bin reaches the top of the range) by its next 8 bits: a
+// histogram over the chunk keys in the bin that beat the floor gives the
+// sub-bin holding the need-th best of them.  Narrows [lo_u, hi_u) to it and
+// returns the keys above it inside the old bin.
+__device__ __forceinline__ uint32_t refine_bin(const RowCtx &r, uint32_t &lo_u, uint32_t &hi_u,
+                                               int shift, uint32_t need, uint32_t *hist,
+                                               SelectShared &sh, int tid)
 {
     const int lane = tid & 63;
     hist[tid] = 0u;
     __syncthreads();
-    const float f_lo = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
-    const float f_hi = score_of_orderable(hi_u);
-    const bool top = hi_u == 0u;  // the bin reaches the top of the orderable range
+    const bool top = hi_u == 0u;
+    const uint32_t lo = max(lo_u, r.u_lo);
     constexpr int V = 16;
     constexpr int ROUND = NT * V;
-    auto count = [&](const float (&v)[V], int64_t base) {
+    auto count = [&](const uint32_t (&v)[V], int64_t base) {
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            const float x = v[i];
-            const bool in = base + i < r.len && (!r.filt || x > r.f_floor) && x >= f_lo &&
-                            (top || !(x >= f_hi));
-            hist_add(hist, in, (orderable(x) >> (shift - 8)) & 255u, lane);
+            const uint32_t u = v[i];
+            const bool in = base + i < r.len && u >= lo && (top || u < hi_u);
+            hist_add(hist, in, (u >> (shift - 8)) & 255u, lane);
         }
     };
     // Two buffers rotating by name (unrolled by two), as in collect().
-    float b0[V], b1[V];
+    uint32_t b0[V], b1[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) b0[i] = b1[i] = 0.0f;
+    for (int i = 0; i < V; ++i) b0[i] = b1[i] = 0u;
     const int64_t lane0 = (int64_t)tid * V;
     load16(r.src, r.len, lane0, b0);
     for (int64_t e0 = 0; e0 < r.len; e0 += 2 * ROUND) {
@@ -670,9 +668,9 @@ __device__ __noinline__ int collect_pieces(uint64_t *cand, const RowCtx r, int k
             bool take = false;
             uint64_t key = 0;
             if (e < plen) {
-                const float x = r.src[p0 + e];
-                key = make_key(x, r.c0 + (uint32_t)(p0 + e));
-                take = (!r.filt || x > r.f_floor) && (!full || key > thr);
+                const uint32_t u = r.src[p0 + e];
+                key = ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (r.c0 + (uint32_t)(p0 + e)));
+                take = u >= r.u_lo && (!full || key > thr);
             }
             const uint64_t m = __ballot(take);
             if (m != 0) {  // wave-uniform
@@ -820,8 +818,10 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
     r.src = a.ws + rl * a.clen + split * a.slen;
     r.len = len;
     r.c0 = (uint32_t)c0;
-    r.filt = theta != 0;
-    r.f_floor = score_of_orderable((uint32_t)(theta >> 32));
+    // A full running list admits only scores above its k-th (equal scores
+    // lose to the list's lower indices).  Finite scores stay below
+    // orderable(+inf) = 0xFF800000, so the +1 cannot wrap.
+    r.u_lo = theta != 0 ? (uint32_t)(theta >> 32) + 1u : 0u;
 
     // Chunk-local best k (the partition step), sorted descending, in
     // cand[0..cnt_q).
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
             const ChunkMeta mt = a.meta[vr];
             if (mt.total <= (uint32_t)k) {
                 // Every key that beats the floor (at most k of them).
-                collect<K>(r, -__builtin_inff(), __builtin_inff(), cand, sh, tid, nA, nB);
+                collect<K>(r, r.u_lo, r.u_lo, cand, sh, tid, nA, nB);
                 done = true;
             } else {
                 constexpr int BIN_SHIFT = 32 - kHistBits;  // orderable bits below the bin
@@ -849,11 +849,12 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
                     (void)up;
                 }
                 if (fits) {
-                    // Bin edges as fp32 thresholds (orderable() is monotone;
-                    // bin 0 starts at -inf, the top bin has no upper edge).
-                    const float f_sure = hi_u == 0u ? __builtin_nanf("") : score_of_orderable(hi_u);
-                    const float f_edge = lo_u == 0u ? -__builtin_inff() : score_of_orderable(lo_u);
-                    collect<K>(r, f_sure, f_edge, cand, sh, tid, nA, nB);
+                    // Bin edges as orderable thresholds, raised to the floor.
+                    // The top bin has no upper edge: 0xFFFFFFFF is above
+                    // every finite score, so its keys all go to region B.
+                    const uint32_t eA = max(hi_u == 0u ? 0xFFFFFFFFu : hi_u, r.u_lo);
+                    const uint32_t eB = max(lo_u, r.u_lo);
+                    collect<K>(r, eA, eB, cand, sh, tid, nA, nB);
                     done = true;
                 }
             }

@@ -35,7 +35,7 @@ namespace {
 constexpr int64_t kDefaultBudget = int64_t(2) << 30;
 constexpr int64_t kDefaultChunkCap = 65536;  // single chunk up to this many keys
 constexpr int64_t kDefaultChunk = 65536;
-constexpr int32_t kDefaultTile = 128;
+constexpr int32_t kDefaultTile = 192;  // keys per LDS tile when the caller sets none
 constexpr int64_t kMaxChunk = int64_t(1) << 24;  // keys; chunk offsets stay 32-bit in the kernels
 constexpr int64_t kMaxRowsNoKeys = int64_t(1) << 20;  // rows per pass when no row has a key
 constexpr size_t kAlign = 256;
@@ -119,7 +119,7 @@ int check_args(int64_t S, int64_t T, int32_t H, int32_t D, int32_t m, int64_t k,
         if (opts->chunk_keys < 0 || (opts->chunk_keys % 256) != 0 || opts->chunk_keys > kMaxChunk)
             return CSA_ERR_BAD_OPTION;
         if (opts->key_tile != 0 && opts->key_tile != 64 && opts->key_tile != 128 &&
-            opts->key_tile != 256)
+            opts->key_tile != 192 && opts->key_tile != 256)
             return CSA_ERR_BAD_OPTION;
         if (opts->workspace_budget < 0) return CSA_ERR_BAD_OPTION;
         const int32_t ks = opts->key_splits;
@@ -255,7 +255,7 @@ const char *csa_status_str(int status)
     case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small for one query block";
     case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 4096 or T >= 2^31)";
     case CSA_ERR_HIP: return "HIP call or kernel launch failed";
-    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256 up to 2^24, key_tile one of 64/128/256, key_splits 0 or a power of two up to 64, reserved fields 0";
+    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256 up to 2^24, key_tile one of 64/128/192/256, key_splits 0 or a power of two up to 64, reserved fields 0";
     case CSA_ERR_SCRATCH_TOO_SMALL: return "allocation-free call: one query block needs more scratch than the library's fixed 256 MiB (use a smaller chunk_keys, or csa_indexer_topk with a workspace)";
     default: return "unknown status";
     }

@@ -297,8 +297,9 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     // 32-lane swap pairs the two half-waves, so lane l ends with the score of
     // key 64p + l, summed as (lanes 0-31 share) + (lanes 32-63 share).
     // Branch-free, so that the tile stays one scheduling region: lanes past
-    // the row's last key store into unused slots of the row (tiles never run
-    // past the split, whose length is a multiple of NT) and add 0 to the
+    // the row's last key store into unused slots of the row or, where a
+    // 192-key tile runs past the end of the split (a multiple of 256 keys),
+    // beyond the buffer range, where the store is dropped; they add 0 to the
     // histogram.
     auto finish2 = [&](float pe, float po, int rel0, bool real) {
         const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(pe), __float_as_uint(po),
@@ -541,6 +542,7 @@ int blocks_per_cu_tile(int32_t key_tile)
     switch (key_tile) {
     case 64: return blocks_per_cu_cfg<D, HT, 64, true, 8>();
     case 128: return blocks_per_cu_cfg<D, HT, 128, true, 8>();
+    case 192: return blocks_per_cu_cfg<D, HT, 192, true, 8>();
     case 256: return blocks_per_cu_cfg<D, HT, 256, (D < 128), 8>();
     default: return 0;
     }
@@ -551,10 +553,13 @@ hipError_t launch_bf16_tile(const ScoreArgs &a, int32_t key_tile, hipStream_t s)
 {
     // 8-row workgroups, one per CU; 256-key tiles of 128 dims are
     // single-buffered to stay within 160 KiB next to the 64 KiB of
-    // histograms.  (Two 4-row workgroups per CU were measured slower.)
+    // histograms, while two 192-key tiles (2 x 48 KiB) fill it exactly: the
+    // automatic choice, with a third fewer tile barriers than 128-key tiles.
+    // (Two 4-row workgroups per CU were measured slower.)
     switch (key_tile) {
     case 64: return launch_bf16_cfg<D, HT, 64, true, 8>(a, s);
     case 128: return launch_bf16_cfg<D, HT, 128, true, 8>(a, s);
+    case 192: return launch_bf16_cfg<D, HT, 192, true, 8>(a, s);
     case 256: return launch_bf16_cfg<D, HT, 256, (D < 128), 8>(a, s);
     default: return hipErrorInvalidValue;
     }

@@ -205,7 +205,7 @@ def test_chunk_and_tile_grid_bit_identical():
     say("chunk/tile grid S=%d T=%d k=%d" % (S, T, k))
     o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
     for chunk in (0, 256, 768, 2048):
-        for tile in (64, 128, 256):
+        for tile in (64, 128, 192, 256):
             say("  chunk=%d tile=%d" % (chunk, tile))
             g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, chunk_keys=chunk, key_tile=tile)
             assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
@@ -345,7 +345,7 @@ def _random_config(rng):
     q_pos0 = int(rng.integers(0, 3000)) if rng.random() < 0.5 else 0
     k = int(rng.choice([1, 7, 64, 300, 2048, 2049, 4096]))
     opts = dict(chunk_keys=int(rng.choice([0, 0, 256, 1024])),
-                key_tile=int(rng.choice([0, 64, 128, 256])),
+                key_tile=int(rng.choice([0, 64, 128, 192, 256])),
                 key_splits=int(rng.choice([0, 0, 1, 2, 8])),
                 workspace_budget=int(rng.choice([0, 0, 1, 1 << 20])))
     return dt, S, T, H, D, m, k, q_pos0, opts
@@ -378,7 +378,7 @@ def test_random_configs_bf16_gaussian(case):
     q_pos0 = int(rng.integers(0, 20000)) if rng.random() < 0.5 else 0
     k = int(rng.choice([1, 16, 500, 2048, 3000, 4096]))
     opts = dict(chunk_keys=int(rng.choice([0, 0, 4096, 16384])),
-                key_tile=int(rng.choice([0, 64, 128, 256])),
+                key_tile=int(rng.choice([0, 64, 128, 192, 256])),
                 key_splits=int(rng.choice([0, 0, 1, 4, 16])),
                 workspace_budget=int(rng.choice([0, 0, 1 << 24])))
     say("gaussian case %d: S=%d T=%d m=%d k=%d q_pos0=%d %s" % (case, S, T, m, k, q_pos0, opts))
@@ -568,6 +568,7 @@ def test_full_size_chunk_and_tile_grid_integer_bit_exact():
     qd, wd, kd = q.to(DEV), w.to(DEV), kc.to(DEV)
     settings = [dict(chunk_keys=c, key_tile=t) for c in (4096, 8192, 16384, 32768, 65536)
                 for t in (64, 128, 256)]
+    settings += [dict(chunk_keys=c, key_tile=192) for c in (4096, 65536)]
     settings += [dict(), dict(key_splits=1), dict(key_splits=4), dict(key_splits=64)]
     for kw in settings:
         say("  %s" % kw)

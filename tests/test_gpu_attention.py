@@ -84,21 +84,44 @@ def test_no_entries_at_all():
     assert torch.all(out == 0)
 
 
-def test_growing_logits_move_the_reference_max():
-    """Entries ordered by rising logit and a large scale: each tile's max
-    rises by far more than the lazy-rescale threshold, so the accumulators
-    are rescaled again and again; a single dominant entry at the end must
-    win."""
+@pytest.mark.parametrize("sign", [1.0, -1.0])
+def test_growing_logits_move_the_reference_max(sign):
+    """Entries ordered so that the scaled logit rises (by logit for a
+    positive scale, against it for a negative one) and a large scale: each
+    tile's max rises by far more than the lazy-rescale threshold, so the
+    accumulators are rescaled again and again; a single dominant entry at
+    the end must win."""
     S, T, H, DK, DV, k = 8, 4096, 64, 576, 512, 512
+    say("attention growing logits, scale sign %+g" % sign)
     q, kv = inputs.attention_gaussian(S, T, H, DK, seed=9)
     rng = np.random.default_rng(9)
     idx = np.zeros((S, k), dtype=np.int32)
     qf, kf = q.float().numpy(), kv.float().numpy()
     for i in range(S):
         sel = rng.choice(T, k, replace=False)
-        score = (qf[i, 0] @ kf[sel].T)          # head 0's logits
+        score = sign * (qf[i, 0] @ kf[sel].T)   # head 0's scaled logits, up to 0.5
         idx[i] = sel[np.argsort(score)]         # ascending: maxima keep rising
-    run_and_check(q, kv, torch.from_numpy(idx), DV, 0.5)
+    run_and_check(q, kv, torch.from_numpy(idx), DV, 0.5 * sign)
+
+
+@pytest.mark.parametrize("H", [32, 64])
+@pytest.mark.parametrize("dims", [(576, 512), (128, 128)])
+@pytest.mark.parametrize("scale_mul", [-1.0, -0.0, 0.0])
+def test_negative_and_zero_scale(H, dims, scale_mul):
+    """Any finite scale is legal.  A negative one favours the smallest
+    logits (the 8-wave kernel moves its sign into q, an exact flip); a zero
+    one gives every selected entry the same weight, so a row's output is the
+    mean of its values.  Both against the oracle, with padding, a row with
+    nothing selected and ragged tiles."""
+    DK, DV = dims
+    S, T, k = 23, 1500, 130
+    say("attention H=%d dk=%d scale x %r" % (H, DK, scale_mul))
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=41 + H + DK)
+    idx = random_selection(np.random.default_rng(41 + H), S, T, k)
+    idx[0, :] = -1
+    scale = scale_mul * 2.0 / DK ** 0.5
+    g, _ = run_and_check(q, kv, idx, DV, scale)
+    assert np.all(g[0] == 0.0)
 
 
 def test_indexer_selection_feeds_attention():

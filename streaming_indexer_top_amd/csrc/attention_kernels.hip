@@ -536,9 +536,13 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
     // Output wave: quarter dq of dv.
     const int dq = wave & 3;
 
-    // Entries past k read the last index (masked where used); with k = 0
-    // there is no index to read.
-    auto load_idx = [&](int t) -> int { return k > 0 ? irow[min(t * kTile + col, k - 1)] : -1; };
+    // The row's indices through a buffer resource that ends after its k
+    // entries: entries past k (and every entry when k = 0) read 0, which the
+    // gather's validity test masks by position.
+    const __amdgpu_buffer_rsrc_t idx_rs = buffer_rsrc(irow, (uint32_t)k * 4u);
+    auto load_idx = [&](int t) -> int {
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(idx_rs, col * 4, t * kTile * 4, 0);
+    };
     // Steps 0 .. ntiles, none without entries (the same count in both roles).
     const int nsteps = ntiles > 0 ? ntiles + 1 : 0;
     const __amdgpu_buffer_rsrc_t kv_rs = buffer_rsrc(a.kv, (uint32_t)(a.T * ROWB));
@@ -553,12 +557,15 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
         g_chunk[j] = j < npw ? (((pos % ROWB) >> 4) ^ sw8(r)) * 16 : 0;
     }
     // The gather of tile t into dst: each wave issues its NP pieces (rows
-    // past k and padding read zeros through the buffer range check).
-    auto gdma = [&](auto lg, unsigned char *dst, int iv, int t) {
+    // past k and padding read zeros through the buffer range check).  Returns
+    // the tile's mask of valid entries (bit e: entry e of the tile selects a
+    // row of kv).
+    auto gdma = [&](auto lg, unsigned char *dst, int iv, int t) -> uint32_t {
         constexpr bool LG = decltype(lg)::value;  // a logit wave's pieces
         constexpr int NP = LG ? PL : PO;
         const int lim = k - t * kTile;
-        const int eoff = (iv >= 0 && iv < nkv && col < lim) ? iv * ROWB : (int)0x80000000;
+        const bool valid = iv >= 0 && iv < nkv && col < lim;
+        const int eoff = valid ? iv * ROWB : (int)0x80000000;
         int e[NP];
 #pragma unroll
         for (int j = 0; j < NP; ++j) e[j] = __builtin_amdgcn_ds_bpermute(g_row[j], eoff);
@@ -567,6 +574,7 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
             const int p = LG ? j * 4 + wave : 4 * PL + j * 4 + (wave - 4);
             dma16(kv_rs, dst + p * 1024, e[j] + g_chunk[j]);
         }
+        return (uint32_t)__ballot(valid);
     };
     const std::true_type pl{};
     const std::false_type po{};
@@ -704,11 +712,13 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
             lds_store_b64(&pT[par][hb][col][16 * kh + 8 + 4 * half], pw1);
             if (lane == 0) flag_s[par][wave] = wave_need ? 1 : 0;
         };
-        // ivs: idx of tile s, replaced by idx of tile s+3; ivg: idx of tile s+2.
-        auto step = [&](const unsigned char *tq, unsigned char *dst, int &ivs, int ivg, int st) {
-            const uint32_t vmask = (uint32_t)__ballot(ivs >= 0 && ivs < nkv && st * kTile + col < k);
+        // ivs: idx of tile s, replaced by idx of tile s+3; ivg: idx of tile
+        // s+2; vmask: valid-entry mask of tile s; vnext receives that of tile
+        // s+2 (the masks rotate through three slots, tile t in slot t % 3).
+        auto step = [&](const unsigned char *tq, unsigned char *dst, int &ivs, int ivg, uint32_t vmask,
+                        uint32_t &vnext, int st) {
             ivs = load_idx(st + 3);
-            gdma(pl, dst, ivg, st + 2);
+            vnext = gdma(pl, dst, ivg, st + 2);
             if (st < ntiles) {
                 const bool more = st + 1 < ntiles;
                 f32x16 acc;  // written and read only when more
@@ -719,20 +729,21 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
             vm_wait<0>();
             lds_barrier();
         };
+        uint32_t vm0 = 0, vm1 = 0, vm2 = 0;  // valid-entry masks of tiles 0, 1, 2 (mod 3)
         if (ntiles > 0) {
-            gdma(pl, tile0, iv0, 0);
-            gdma(pl, tile1, iv1, 1);
+            vm0 = gdma(pl, tile0, iv0, 0);
+            vm1 = gdma(pl, tile1, iv1, 1);
             vm_wait<0>();
         }
         __syncthreads();
         if (ntiles > 0) publish(qk(tile0), 0);
         __syncthreads();
         for (int st = 0; st < nsteps; st += 3) {
-            step(tile1, tile2, iv0, iv2, st);
+            step(tile1, tile2, iv0, iv2, vm0, vm2, st);
             if (st + 1 >= nsteps) break;
-            step(tile2, tile0, iv1, iv0, st + 1);
+            step(tile2, tile0, iv1, iv0, vm1, vm0, st + 1);
             if (st + 2 >= nsteps) break;
-            step(tile0, tile1, iv2, iv1, st + 2);
+            step(tile0, tile1, iv2, iv1, vm2, vm1, st + 2);
         }
         // Denominators: sum each head's per-lane shares over the 32 lanes of
         // a half.

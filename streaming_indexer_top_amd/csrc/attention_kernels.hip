@@ -13,7 +13,10 @@
 //
 // sel(i) = idx[i,:] without its -1 padding; an empty selection gives zeros.
 //
-// One workgroup per query row, 4 waves per 32-head block.  Wave (hb, qq)
+// Two kernels, one workgroup per query row each.  For 64 heads,
+// attention_split_kernel (further down) gives half of its 8 waves the logits
+// and softmax and the other half P * V, one barrier per 32-entry tile.  For
+// 32 heads, attention_kernel runs 4 waves per 32-head block.  Wave (hb, qq)
 // keeps its heads' q for k-steps qq*KQ .. qq*KQ+KQ-1 resident (a quarter of
 // dk), so every wave of a head block computes a partial 32x32 logit block per
 // 32-entry tile with v_mfma_f32_32x32x16_bf16; the four partials meet in LDS.

@@ -13,36 +13,22 @@
 //
 // sel(i) = idx[i,:] without its -1 padding; an empty selection gives zeros.
 //
-// Two kernels, one workgroup per query row each.  For 64 heads,
-// attention_split_kernel (further down) gives half of its 8 waves the logits
-// and softmax and the other half P * V, one barrier per 32-entry tile.  For
-// 32 heads, attention_kernel runs 4 waves per 32-head block.  Wave (hb, qq)
-// keeps its heads' q for k-steps qq*KQ .. qq*KQ+KQ-1 resident (a quarter of
-// dk), so every wave of a head block computes a partial 32x32 logit block per
-// 32-entry tile with v_mfma_f32_32x32x16_bf16; the four partials meet in LDS.
-// The selected latent rows are gathered by LDS DMA into the free one of
-// three static tile buffers: each lane moves the 16 bytes its slot of the
-// swizzled tile needs, straight from the row the index names (-1 reads
-// zeros through the buffer range check).  The gather of tile t+2 starts at
-// the beginning of tile step t and has until the end of that step.  The
-// barriers inside the loop carry no memory fence (a fence would wait for
-// every DMA in flight); the wait for a tile's DMAs is an explicit vmcnt
-// before the barrier that publishes it.  Tile step t has
-// two intervals between barriers:
-//   1. wave qq of a head block finishes 8 of its 32 heads for tile t: sums
-//      the four partial logit quarters in a fixed order, masks padding and
-//      runs an online softmax in base 2 whose reference max moves only when
-//      a head's max rises by more than 2^8 (the factor then rescales the
-//      accumulators; otherwise they are left alone), and writes P (bf16,
-//      transposed: one 8-byte store per lane) to LDS; under this vector
-//      work the same waves' MFMAs compute the partial logits of tile t+1
-//      (B fragments from the tile),
-//   2. the partials of tile t+1 go to LDS, and P * V of tile t runs with
-//      v_mfma_f32_32x32x16_bf16, wave qq owning a quarter of the dv output
-//      dims: the V fragments (8 consecutive entries of one dim per lane)
-//      come from the row-major tile by ds_read_b64_tr_b16, two transposing
-//      8-byte reads per fragment.
-// The softmax denominators are kept per lane and reduced once at the end.
+// One workgroup of 8 waves per query row (attention_split_kernel below, for
+// 32 and 64 heads).  Four logit waves compute the logits of a 32-entry tile
+// with v_mfma_f32_32x32x16_bf16 (q resident in registers, each wave over a
+// range of the dk k-steps), exchange partial logit blocks in LDS and run an
+// online softmax in base 2 whose reference max moves only when a head's max
+// rises by more than 2^8; four output waves accumulate P * V, each over a
+// quarter of the dv output dims, with the V fragments taken from the
+// row-major tile by transposing LDS reads (ds_read_b64_tr_b16).  The
+// selected latent rows are gathered by LDS DMA into the free one of three
+// static tile buffers: each lane moves the 16 bytes its slot of the swizzled
+// tile needs, straight from the row the index names (padding and indices
+// outside [0, T) read zeros through the buffer range check).  The barriers
+// inside the loop carry no memory fence (a fence would wait for every DMA in
+// flight); the wait for a tile's DMAs is an explicit vmcnt before the barrier
+// that publishes it.  The softmax denominators are kept per lane and reduced
+// once at the end.
 #include "csa_internal.h"
 
 #include <type_traits>
@@ -167,340 +153,42 @@ __device__ inline void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int 
                                             off, 0, 0, 0);
 }
 
-template <int DK, int DV, int HB>
-__global__ __launch_bounds__(256 * HB) void attention_kernel(AttnArgs a)
-{
-    constexpr int WAVES = 4 * HB;
-    constexpr int KQ = DK / 64;         // 16-dim k-steps per quarter of dk
-    constexpr int NBW = DV / 128;       // 32-dim output blocks per wave
-    constexpr int ROWB = DK * 2;        // bytes per latent row
-    constexpr int TILEB = kTile * ROWB; // bytes per tile
-    constexpr int NPIECE = TILEB / 1024;
-    constexpr int PPW = (NPIECE + WAVES - 1) / WAVES;  // DMA pieces per wave
-    static_assert(DK % 64 == 0 && DV % 128 == 0 && DV <= DK, "shape");
-    static_assert(TILEB % 1024 == 0 && (DK / 8) % 8 == 0, "whole DMA pieces, 8-chunk swizzle");
-
-    __shared__ __attribute__((aligned(16))) unsigned char tile0[TILEB];
-    __shared__ __attribute__((aligned(16))) unsigned char tile1[TILEB];
-    __shared__ __attribute__((aligned(16))) unsigned char tile2[TILEB];
-    // part[w][r-1]: quad r (r = 1..3) of wave w's partial logits, for the
-    // wave of its head block that finishes those heads.
-    __shared__ __attribute__((aligned(16))) f32x4 part[WAVES][3][64];
-    // P transposed: pT[hb][entry][head], read as the A fragments of P * V
-    // by the same transposing loads as the value fragments.
-    __shared__ __attribute__((aligned(16))) __bf16 pT[HB][kTile][kPRow];
-    __shared__ __attribute__((aligned(16))) float alpha_s[HB * 32];
-    __shared__ __attribute__((aligned(16))) float l_s[HB * 32];
-    __shared__ __attribute__((aligned(16))) int flag_s[WAVES];
-    __shared__ __attribute__((aligned(16))) unsigned char sink[1024];  // target of the spare DMAs
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hb = wave >> 2, qq = wave & 3;
-    const int col = lane & 31, half = lane >> 5;
-    const int64_t row = blockIdx.x;
-    const int k = a.k;
-    const int ntiles = (k + kTile - 1) / kTile;
-    const int32_t *irow = a.idx + row * (int64_t)k;
-    const int nkv = (int)a.T;  // an index outside [0, T) counts as padding
-
-    // Resident q, heads rotated by 8*qq: A row r of this wave is head
-    // hb*32 + (r + 8qq) % 32, so accumulator quad 0 (rows 4half .. 4half+3)
-    // holds the heads this wave finishes (8qq + 4half + ii) and quad r the
-    // heads of wave (qq + r) % 4.  Dims (qq*KQ + j)*16 + half*8 .. +7.
-    bf16x8 qf[KQ];
-    {
-        const int head = hb * 32 + ((col + 8 * qq) & 31);
-        const __bf16 *qh = (const __bf16 *)a.q + ((int64_t)row * a.H + head) * DK;
-#pragma unroll
-        for (int j = 0; j < KQ; ++j) qf[j] = *(const bf16x8 *)(qh + (qq * KQ + j) * 16 + half * 8);
-    }
-    // Wait for q here, ahead of the gather loads: otherwise the compiler
-    // may place that wait in the tile loop, where it also waits for the
-    // gather loads in flight.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-
-    // Entry index of tile row (lane % 32) of tile t; rows past k read the
-    // last index (a valid address) and are masked where used.
-    auto load_idx = [&](int t) -> int { return irow[min(t * kTile + col, k - 1)]; };
-    // Gather of one tile: piece p of the tile is 1 KiB; its lane l holds
-    // bytes [16l, 16l+16) of the piece, i.e. row r, slot s of the tile,
-    // which is chunk s ^ sw8(r) of latent row idx[r] (the swizzle spreads a
-    // B-fragment read over the banks).  Per piece the lane's row (as a
-    // bpermute byte address) and chunk byte offset are fixed for the row.
-    const __amdgpu_buffer_rsrc_t kv_rs = buffer_rsrc(a.kv, (uint32_t)(a.T * ROWB));
-    int g_row[PPW], g_chunk[PPW];
-#pragma unroll
-    for (int j = 0; j < PPW; ++j) {
-        const int pos = (j * WAVES + wave) * 1024 + lane * 16;
-        const int r = (pos / ROWB) & 31;  // pieces past the tile (p >= NPIECE) go to the sink
-        g_row[j] = r * 4;
-        // Spare pieces (the sink's) get an offset that is out of range for
-        // any real row.
-        g_chunk[j] = j * WAVES + wave < NPIECE ? (((pos % ROWB) >> 4) ^ sw8(r)) * 16 : (int)0x80000000;
-    }
-    // DMA gather of tile t into dst, rows from iv (idx of tile t).  Every
-    // wave issues exactly PPW DMAs per call, whatever t: pieces past the
-    // tile go to the sink, rows past k (all of them for t >= ntiles) read
-    // zeros, so the count of memory ops in flight is the same on every
-    // path and the waits can count on it.
-    auto gdma = [&](unsigned char *dst, int iv, int t) {
-        const int lim = k - t * kTile;  // rows r >= lim are past k
-        // Byte offset of this lane's row (lane % 32); a negative index, or a
-        // row past k, gets bit 31: out of the buffer's range, so the DMAs of
-        // that row write zeros.
-        const int eoff = (iv >= 0 && iv < nkv && col < lim) ? iv * ROWB : (int)0x80000000;
-        int e[PPW];
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) e[j] = __builtin_amdgcn_ds_bpermute(g_row[j], eoff);
-#pragma unroll
-        for (int j = 0; j < PPW; ++j) {
-            const int p = j * WAVES + wave;
-            dma16(kv_rs, p < NPIECE ? dst + p * 1024 : sink, e[j] + g_chunk[j]);
-        }
-    };
-    f32x16 o[NBW];
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) o[nb] = f32x16{};
-    // Reference max, the threshold mref + kTau and the per-lane denominators
-    // of heads 8qq + 4half + ii.
-    float mref[4], thr[4], lsum[4];
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        mref[ii] = -__builtin_inff();
-        thr[ii] = -__builtin_inff();
-        lsum[ii] = 0.0f;
-    }
-    const float c2 = a.scale_log2e;
-
-    // Per-lane byte offsets inside a tile, fixed for the whole row.
-    // Logit B fragments: entry col, chunk 2*(qq*KQ + j) + half, swizzled.
-    int qk_off[KQ];
-#pragma unroll
-    for (int j = 0; j < KQ; ++j)
-        qk_off[j] = col * ROWB + (((2 * (qq * KQ + j) + half) ^ sw8(col)) << 4);
-    // Value fragments read by the transposing loads: this lane points at
-    // entry kk*16 + eb + 4*s2 (s2: first or second half of its 8 entries),
-    // dims dl..dl+3 of output block nb; inside a tile that is byte
-    //   kk*16*ROWB + hi(nb) + tr_off[s2][parity(nb)]
-    // where hi(nb) is the 128-byte group of the block's chunks and the
-    // parity picks which half of that group, which the swizzle (sw8(entry))
-    // permutes per lane.
-    const int eb = ((lane >> 5) * 8) + ((lane & 15) >> 2);
-    const int dl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    const int cq = qq * (DV / 32);  // first output chunk of this wave
-    int tr_off[2][2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        const int e = eb + 4 * s2;
-#pragma unroll
-        for (int par = 0; par < 2; ++par) {
-            const int bp = ((cq >> 2) + par) & 1;  // bit 2 of the block's first chunk
-            tr_off[s2][par] = e * ROWB + (((bp * 4 + (dl >> 3)) ^ sw8(e)) << 4) + (dl & 7) * 2;
-        }
-    }
-
-    // Logits of tile t+1 are computed during the softmax of tile t: the
-    // MFMAs run while the same waves do the vector work.  acc holds them
-    // from the first interval of a step to the second; own keeps this
-    // wave's quarter of its own heads (quad 0) for the next softmax.
-    f32x16 acc = {};
-    f32x4 own = {};
-    auto qk = [&](const unsigned char *tb) {
-        acc = f32x16{};
-#pragma unroll
-        for (int j = 0; j < KQ; ++j) {
-            const bf16x8 b = *(const bf16x8 *)(tb + qk_off[j]);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[j], b, acc, 0, 0, 0);
-        }
-    };
-    auto write_parts = [&]() {
-        own = f32x4{acc[0], acc[1], acc[2], acc[3]};
-#pragma unroll
-        for (int r4 = 1; r4 < 4; ++r4)  // quad 0 stays: this wave finishes those heads
-            part[wave][r4 - 1][lane] = f32x4{acc[4 * r4], acc[4 * r4 + 1], acc[4 * r4 + 2], acc[4 * r4 + 3]};
-    };
-
-    // Step t, two intervals.  First: the idx of tile t+3 and the gather of
-    // tile t+2 (into the buffer tile t-1 left), this wave's logit sums of
-    // tile t (own quarter, then waves qq+1, qq+2, qq+3: a fixed order), the
-    // logit MFMAs of tile t+1, and the softmax of tile t (P, factors and
-    // flag to LDS).  Second: the partial logits of tile t+1 to LDS, then
-    // O = alpha * O + P V of tile t; the gather of tile t+2 is waited for
-    // before the barrier that ends the step.  tb: tile t; tn: tile t+1;
-    // dst: the buffer of tile t+2; ivc: idx of tile t, replaced by idx of
-    // tile t+3; ivd: idx of tile t+2.
-    auto step = [&](const unsigned char *tb, const unsigned char *tn, unsigned char *dst, int &ivc,
-                    int ivd, int t) {
-        const uint32_t vmask = (uint32_t)__ballot(ivc >= 0 && ivc < nkv && t * kTile + col < k);
-        ivc = load_idx(t + 3);
-        gdma(dst, ivd, t + 2);
-        f32x4 s = own;
-#pragma unroll
-        for (int d = 1; d < 4; ++d) s += part[hb * 4 + ((qq + d) & 3)][3 - d][lane];
-        if (t + 1 < ntiles) qk(tn);
-        const bool valid = (vmask >> col) & 1u;
-        float x[4];
-        bool exceed = false;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            x[ii] = s[ii] * c2;
-            exceed |= x[ii] > thr[ii];
-        }
-        exceed = exceed && valid;
-        // A head's reference max moves only when some logit of the tile
-        // exceeds it by more than kTau; usually none does, and the tile
-        // maxima are not needed at all.
-        const bool wave_need = __ballot(exceed) != 0;  // wave-uniform
-        if (wave_need) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const float mx = half_max(valid ? x[ii] : -__builtin_inff());
-                float alpha = 1.0f;
-                if (mx > thr[ii]) {
-                    alpha = __builtin_amdgcn_exp2f(mref[ii] - mx);
-                    mref[ii] = mx;
-                    thr[ii] = mx + kTau;
-                    lsum[ii] *= alpha;
-                }
-                if (col == 0) alpha_s[hb * 32 + 8 * qq + 4 * half + ii] = alpha;
-            }
-        }
-        i16x4 pw;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            // A present entry has a finite reference max (its logit set
-            // one if none was); an absent one gets 0.
-            const float p = valid ? __builtin_amdgcn_exp2f(x[ii] - mref[ii]) : 0.0f;
-            lsum[ii] += p;
-            pw[ii] = __builtin_bit_cast(short, (__bf16)p);
-        }
-        *(i16x4 *)&pT[hb][col][8 * qq + 4 * half] = pw;
-        if (lane == 0) flag_s[wave] = wave_need ? 1 : 0;
-        lds_barrier();
-        if (t + 1 < ntiles) write_parts();
-        // 3. O = alpha * O + P V for head block hb, dims qq*DV/4 .. +DV/4-1.
-        u32x4 fl;
-        i16x4 t00, t01, t10, t11;
-        lds_read_fp(&flag_s[hb * 4], &pT[hb][eb][dl], &pT[hb][eb + 4][dl], &pT[hb][16 + eb][dl],
-                    &pT[hb][16 + eb + 4][dl], fl, t00, t01, t10, t11);
-        const i16x8 pa0 = {t00[0], t00[1], t00[2], t00[3], t01[0], t01[1], t01[2], t01[3]};
-        const i16x8 pa1 = {t10[0], t10[1], t10[2], t10[3], t11[0], t11[1], t11[2], t11[3]};
-        const bf16x8 pab[2] = {__builtin_bit_cast(bf16x8, pa0), __builtin_bit_cast(bf16x8, pa1)};
-        const bool resc = __builtin_amdgcn_readfirstlane((int)(fl[0] | fl[1] | fl[2] | fl[3])) != 0;  // block-uniform
-        if (resc) {
-#pragma unroll
-            for (int j4 = 0; j4 < 4; ++j4) {
-                // A wave whose flag is clear wrote no factors this tile:
-                // its heads keep 1.
-                f32x4 al = *(const f32x4 *)&alpha_s[hb * 32 + 8 * j4 + 4 * half];
-                if (fl[j4] == 0u) al = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-#pragma unroll
-                for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) o[nb][4 * j4 + ii] *= al[ii];
-            }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 pa = pab[kk];
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int hi = ((cq + nb * 4) & ~7) * 16;  // wave-uniform
-                const unsigned char *vb = tb + kk * 16 * ROWB + hi;
-                const i16x4 v0 = read_tr16(vb + tr_off[0][nb & 1]);
-                const i16x4 v1 = read_tr16(vb + tr_off[1][nb & 1]);
-                const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, __builtin_bit_cast(bf16x8, vv),
-                                                                o[nb], 0, 0, 0);
-            }
-        }
-        vm_wait<0>();
-        lds_barrier();
-    };
-
-    // Tiles rotate through the three buffers and three idx registers (the
-    // loop is unrolled by three so that every access names its buffer).
-    int iv0 = -1, iv1 = -1, iv2 = -1;
-    if (ntiles > 0) {
-        iv0 = load_idx(0);
-        iv1 = load_idx(1);
-        iv2 = load_idx(2);
-        gdma(tile0, iv0, 0);
-        gdma(tile1, iv1, 1);
-        vm_wait<0>();
-    }
-    __syncthreads();
-    if (ntiles > 0) {
-        qk(tile0);
-        write_parts();
-    }
-    __syncthreads();
-    for (int t = 0; t < ntiles; t += 3) {
-        step(tile0, tile1, tile2, iv0, iv2, t);
-        if (t + 1 >= ntiles) break;
-        step(tile1, tile2, tile0, iv1, iv0, t + 1);
-        if (t + 2 >= ntiles) break;
-        step(tile2, tile0, tile1, iv2, iv1, t + 2);
-    }
-    __syncthreads();
-
-    // Denominators: sum the per-lane shares of each head over its 32 lanes.
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-        float l = lsum[ii];
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) l += __shfl_xor(l, off);
-        if (col == 0) l_s[hb * 32 + 8 * qq + 4 * half + ii] = l;
-    }
-    __syncthreads();
-    __bf16 *orow = (__bf16 *)a.out + (int64_t)row * a.H * DV;
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-        const f32x4 l4 = *(const f32x4 *)&l_s[hb * 32 + 8 * j4 + 4 * half];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int head = hb * 32 + 8 * j4 + 4 * half + ii;
-            const float inv = l4[ii] > 0.0f ? 1.0f / l4[ii] : 0.0f;
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                const int dim = qq * (DV / 4) + nb * 32 + col;
-                orow[(int64_t)head * DV + dim] = (__bf16)(o[nb][4 * j4 + ii] * inv);
-            }
-        }
-    }
-}
-
-// Role-split form for 64 heads: one workgroup of 8 waves per query row and
-// one barrier per 32-entry tile step.  Waves w and w+4 of a workgroup share a
-// SIMD, so every SIMD runs one logit wave and one output wave.
-//   Logit waves 0..3: wave (hb, kh) keeps q of head block hb (32 heads) for
-//   half kh of the dk k-steps and computes a partial 32x32 logit block per
-//   tile (one MFMA chain).  Its A rows are rotated by 16*kh so that
-//   accumulator quads 0 and 1 hold the 16 heads it finishes; quads 2 and 3
-//   (its partner's heads) go to LDS.  In the next step it adds the partner's
-//   half (a fixed order: own + partner), runs the online softmax in base 2
-//   with a lazily moved reference max (as in attention_kernel), and writes P
-//   (bf16, entry-major) and its rescale factors and flag.
-//   Output waves 4..7: wave j owns dims j*dv/4 .. +dv/4-1 for all 64 heads
-//   (128 accumulator registers at dv = 512).  In step s it rescales O when a
-//   flag of tile s-1 is set and adds P(s-1) * V(s-1), V from registers, each
-//   value fragment feeding both head blocks; then it loads V(s) from the
-//   tile by transposing LDS reads.
+// Role-split attention for HB head blocks of 32 heads (HB = 1 or 2): one
+// workgroup of 8 waves per query row and one barrier per 32-entry tile step.
+// Waves w and w+4 of a workgroup share a SIMD, so every SIMD runs one logit
+// wave and one output wave.
+//   Logit waves 0..3: wave (hb, ksp) keeps q of head block hb for k-step
+//   range ksp (of NSPLIT = 4/HB ranges) and computes a partial 32x32 logit
+//   block per tile (one MFMA chain).  Its A rows are rotated by 8*QPW*ksp
+//   (QPW = 4/NSPLIT) so that accumulator quads 0 .. QPW-1 hold the 8*QPW
+//   heads it finishes; its other quads go to LDS for the waves that finish
+//   those heads.  In the next step it adds the other waves' partials to its
+//   own (in a fixed order), runs the online softmax in base 2 with a lazily
+//   moved reference max, and writes P (bf16, entry-major) and its rescale
+//   factors and flag.
+//   Output waves 4..7: wave j owns dims j*dv/4 .. +dv/4-1 for all heads
+//   (64*HB accumulator registers at dv = 512).  In step s it rescales O when
+//   a flag of tile s-1 is set and adds P(s-1) * V(s-1), V from registers,
+//   each value fragment feeding every head block; then it loads V(s) from
+//   the tile by transposing LDS reads.
 // Step s: logits of tile s+1, softmax of tile s, P*V of tile s-1, gather of
 // tile s+2 (into the buffer of tile s-1, free since step s-1).  The partial
 // logits, P, factors and flags are double-buffered by step parity; the
 // single barrier at the end of a step publishes them and the gathered tile.
 // The logit MFMAs of a step are issued before its softmax: measured, that
 // order is faster than the reverse.
-template <int DK, int DV>
+template <int DK, int DV, int HB>
 __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
 {
-    constexpr int WAVES = 8;
+    constexpr int NH = 32 * HB;         // heads
+    constexpr int NSPLIT = 4 / HB;      // logit waves per head block, one k-step range each
+    constexpr int QPW = 4 / NSPLIT;     // accumulator quads (8 heads each) a logit wave finishes
+    constexpr int NV = 4 * QPW;         // softmax values per lane of a logit wave
     constexpr int KS = DK / 16;         // 16-dim k-steps over dk
-    constexpr int KH = KS / 2;          // k-steps per logit wave
+    constexpr int KH = KS / NSPLIT;     // k-steps per logit wave
     constexpr int NBW = DV / 128;       // 32-dim output blocks per output wave
+    static_assert(HB == 1 || HB == 2, "32 or 64 heads");
+    static_assert(KS % NSPLIT == 0, "whole k-step ranges");
     constexpr int ROWB = DK * 2;
     constexpr int TILEB = kTile * ROWB;
     constexpr int NPIECE = TILEB / 1024;
@@ -516,12 +204,13 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
     __shared__ __attribute__((aligned(16))) unsigned char tile0[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char tile1[TILEB];
     __shared__ __attribute__((aligned(16))) unsigned char tile2[TILEB];
-    // part[parity][logit wave][quad 2, 3]: the partner's half of a partial logit block.
-    __shared__ __attribute__((aligned(16))) f32x4 part[2][4][2][64];
-    __shared__ __attribute__((aligned(16))) __bf16 pT[2][2][kTile][kPRow];
-    __shared__ __attribute__((aligned(16))) float alpha_s[2][64];
+    // part[parity][logit wave][quad QPW .. 3]: the quads of a partial logit
+    // block whose heads other waves finish.
+    __shared__ __attribute__((aligned(16))) f32x4 part[2][4][4 - QPW][64];
+    __shared__ __attribute__((aligned(16))) __bf16 pT[2][HB][kTile][kPRow];
+    __shared__ __attribute__((aligned(16))) float alpha_s[2][NH];
     __shared__ __attribute__((aligned(16))) int flag_s[2][4];
-    __shared__ __attribute__((aligned(16))) float l_s[64];
+    __shared__ __attribute__((aligned(16))) float l_s[NH];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -534,8 +223,8 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
     const int32_t *irow = a.idx + row * (int64_t)k;
     const int nkv = (int)a.T;
 
-    // Logit wave: head block hb, k-step half kh.
-    const int hb = (wave >> 1) & 1, kh = wave & 1;
+    // Logit wave: head block hb, k-step range ksp (of NSPLIT).
+    const int hb = (wave & 3) / NSPLIT, ksp = (wave & 3) % NSPLIT;
     // Output wave: quarter dq of dv.
     const int dq = wave & 3;
 
@@ -599,13 +288,13 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
         iv2 = load_idx(2);
     }
     if (logit) {
-        // ---- logit wave (hb, kh) ----
+        // ---- logit wave (hb, ksp) ----
         bf16x8 qf[KH];
         {
-            const int head = hb * 32 + ((col + 16 * kh) & 31);
-            const __bf16 *qh = (const __bf16 *)a.q + ((int64_t)row * 64 + head) * DK;
+            const int head = hb * 32 + ((col + 8 * QPW * ksp) & 31);
+            const __bf16 *qh = (const __bf16 *)a.q + ((int64_t)row * NH + head) * DK;
 #pragma unroll
-            for (int j = 0; j < KH; ++j) qf[j] = *(const bf16x8 *)(qh + (kh * KH + j) * 16 + half * 8);
+            for (int j = 0; j < KH; ++j) qf[j] = *(const bf16x8 *)(qh + (ksp * KH + j) * 16 + half * 8);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q before the gather loads
         // The softmax works on raw logits s with the scale c folded into the
@@ -618,17 +307,19 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
             for (int j = 0; j < KH; ++j)
                 qf[j] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qf[j]) ^ 0x80008000u);
         }
-        // B fragment j (k-step kh*KH + j) of an entry row is chunk
-        // c = 2*(kh*KH + j) + half, stored at chunk c ^ sw8(col); the swizzle
+        // B fragment j (k-step ksp*KH + j) of an entry row is chunk
+        // c = 2*(ksp*KH + j) + half, stored at chunk c ^ sw8(col); the swizzle
         // only touches the low three bits of c, so for j = 4m + r the offset
         // is qb[r] + 128*m, an immediate in the read.
         int qb[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) qb[r] = col * ROWB + (((2 * (kh * KH + r) + half) ^ sw8(col)) << 4);
-        f32x4 own0 = {}, own1 = {};  // quads 0, 1 of the next tile's partial logits
-        float mref[8], thr[8], lsum[8];  // mref: scaled (s*c); thr: raw logit units
+        for (int r = 0; r < 4; ++r) qb[r] = col * ROWB + (((2 * (ksp * KH + r) + half) ^ sw8(col)) << 4);
+        f32x4 own[QPW];  // quads 0 .. QPW-1 of the next tile's partial logits
 #pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
+        for (int oq = 0; oq < QPW; ++oq) own[oq] = f32x4{};
+        float mref[NV], thr[NV], lsum[NV];  // mref: scaled (s*c); thr: raw logit units
+#pragma unroll
+        for (int ii = 0; ii < NV; ++ii) {
             mref[ii] = -__builtin_inff();
             thr[ii] = -__builtin_inff();
             lsum[ii] = 0.0f;
@@ -661,32 +352,40 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
             return c;
         };
         auto publish = [&](const f32x16 &acc, int par) {
-            own0 = f32x4{acc[0], acc[1], acc[2], acc[3]};
-            own1 = f32x4{acc[4], acc[5], acc[6], acc[7]};
-            part[par][wave][0][lane] = f32x4{acc[8], acc[9], acc[10], acc[11]};
-            part[par][wave][1][lane] = f32x4{acc[12], acc[13], acc[14], acc[15]};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 v = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+                if (q < QPW) own[q] = v;
+                else part[par][wave][q - QPW][lane] = v;
+            }
         };
-        // Softmax of a tile: own partial quads + the partner's, masked by
-        // vmask; P, factors and flag to pT/alpha_s/flag_s[par].
+        // Softmax of a tile: own partial quads + the other waves' of the head
+        // block (in the fixed order ksp+1, ksp+2, ... mod NSPLIT), masked by
+        // vmask; P, factors and flag to pT/alpha_s/flag_s[par].  Partner ks'
+        // keeps the rows of own quad oq in its quad (QPW*(ksp - ks') + oq) mod 4.
         auto softmax = [&](int par, uint32_t vmask) {
-            const f32x4 p0 = part[par][wave ^ 1][0][lane];
-            const f32x4 p1 = part[par][wave ^ 1][1][lane];
-            const f32x4 s0 = own0 + p0, s1 = own1 + p1;
             const bool valid = (vmask >> col) & 1u;
-            float x[8];
+            float x[NV];
             bool exceed = false;
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                x[ii] = s0[ii];
-                x[4 + ii] = s1[ii];
+            for (int oq = 0; oq < QPW; ++oq) {
+                f32x4 sq = own[oq];
+#pragma unroll
+                for (int d = 1; d < NSPLIT; ++d) {
+                    const int ks2 = (ksp + d) % NSPLIT;
+                    const int qp = (QPW * (ksp - ks2) + oq) & 3;
+                    sq += part[par][hb * NSPLIT + ks2][qp - QPW][lane];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) x[4 * oq + i] = sq[i];
             }
 #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) exceed |= x[ii] > thr[ii];
+            for (int ii = 0; ii < NV; ++ii) exceed |= x[ii] > thr[ii];
             exceed = exceed && valid;
             const bool wave_need = __ballot(exceed) != 0;  // wave-uniform
             if (wave_need) {
 #pragma unroll
-                for (int ii = 0; ii < 8; ++ii) {
+                for (int ii = 0; ii < NV; ++ii) {
                     const float mx = half_max(valid ? x[ii] : -__builtin_inff());
                     float alpha = 1.0f;
                     if (mx > thr[ii]) {
@@ -697,22 +396,22 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
                         lsum[ii] *= alpha;
                     }
                     // accumulator row 8*(ii/4) + 4*half + ii%4 of the rotated
-                    // block is head hb*32 + 16*kh + that row
+                    // block is head hb*32 + 8*QPW*ksp + that row
                     if (col == 0)
-                        lds_store_b32(&alpha_s[par][hb * 32 + 16 * kh + 8 * (ii >> 2) + 4 * half + (ii & 3)],
+                        lds_store_b32(&alpha_s[par][hb * 32 + 8 * QPW * ksp + 8 * (ii >> 2) + 4 * half + (ii & 3)],
                                       alpha);
                 }
             }
-            i16x4 pw0, pw1;
+            i16x4 pw[QPW];
 #pragma unroll
-            for (int ii = 0; ii < 8; ++ii) {
+            for (int ii = 0; ii < NV; ++ii) {
                 const float pp = valid ? __builtin_amdgcn_exp2f(__builtin_fmaf(x[ii], c2, -mref[ii])) : 0.0f;
                 lsum[ii] += pp;
-                if (ii < 4) pw0[ii] = __builtin_bit_cast(short, (__bf16)pp);
-                else pw1[ii - 4] = __builtin_bit_cast(short, (__bf16)pp);
+                pw[ii >> 2][ii & 3] = __builtin_bit_cast(short, (__bf16)pp);
             }
-            lds_store_b64(&pT[par][hb][col][16 * kh + 4 * half], pw0);
-            lds_store_b64(&pT[par][hb][col][16 * kh + 8 + 4 * half], pw1);
+#pragma unroll
+            for (int oq = 0; oq < QPW; ++oq)
+                lds_store_b64(&pT[par][hb][col][8 * QPW * ksp + 8 * oq + 4 * half], pw[oq]);
             if (lane == 0) flag_s[par][wave] = wave_need ? 1 : 0;
         };
         // ivs: idx of tile s, replaced by idx of tile s+3; ivg: idx of tile
@@ -751,18 +450,18 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
         // Denominators: sum each head's per-lane shares over the 32 lanes of
         // a half.
 #pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
+        for (int ii = 0; ii < NV; ++ii) {
             float l = lsum[ii];
 #pragma unroll
             for (int off = 1; off < 32; off <<= 1) l += __shfl_xor(l, off);
-            if (col == 0) l_s[hb * 32 + 16 * kh + 8 * (ii >> 2) + 4 * half + (ii & 3)] = l;
+            if (col == 0) l_s[hb * 32 + 8 * QPW * ksp + 8 * (ii >> 2) + 4 * half + (ii & 3)] = l;
         }
         __syncthreads();
     } else {
         // ---- output wave dq ----
-        f32x16 o[2][NBW];
+        f32x16 o[HB][NBW];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < HB; ++h)
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) o[h][nb] = f32x16{};
         const int eb = ((lane >> 5) * 8) + ((lane & 15) >> 2);
@@ -801,14 +500,15 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
                         &pT[par][0][16 + eb][dl], &pT[par][0][16 + eb + 4][dl], fl, t00, t01, t10, t11);
             const bool resc = __builtin_amdgcn_readfirstlane((int)(fl[0] | fl[1] | fl[2] | fl[3])) != 0;
             if (resc) {
-                // Heads hb*32 + 16*kh .. +15 belong to logit wave 2*hb + kh;
-                // a wave whose flag is clear wrote no factors: its heads keep 1.
+                // Heads h*32 + 8*QPW*ks .. +8*QPW-1 belong to logit wave
+                // h*NSPLIT + ks; a wave whose flag is clear wrote no factors:
+                // its heads keep 1.
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                for (int h = 0; h < HB; ++h)
 #pragma unroll
                     for (int j4 = 0; j4 < 4; ++j4) {
                         f32x4 al = *(const f32x4 *)&alpha_s[par][h * 32 + 8 * j4 + 4 * half];
-                        if (fl[2 * h + (j4 >> 1)] == 0u) al = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+                        if (fl[h * NSPLIT + j4 / QPW] == 0u) al = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
                         for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
@@ -816,10 +516,10 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
                     }
             }
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if (h == 1)
-                    lds_read_fp(&flag_s[par][0], &pT[par][1][eb][dl], &pT[par][1][eb + 4][dl],
-                                &pT[par][1][16 + eb][dl], &pT[par][1][16 + eb + 4][dl], fl, t00, t01,
+            for (int h = 0; h < HB; ++h) {
+                if (h > 0)
+                    lds_read_fp(&flag_s[par][0], &pT[par][h][eb][dl], &pT[par][h][eb + 4][dl],
+                                &pT[par][h][16 + eb][dl], &pT[par][h][16 + eb + 4][dl], fl, t00, t01,
                                 t10, t11);
                 const bf16x8 pa0 = __builtin_bit_cast(
                     bf16x8, i16x8{t00[0], t00[1], t00[2], t00[3], t01[0], t01[1], t01[2], t01[3]});
@@ -854,9 +554,9 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
             lds_barrier();
         }
         __syncthreads();
-        __bf16 *orow = (__bf16 *)a.out + (int64_t)row * 64 * DV;
+        __bf16 *orow = (__bf16 *)a.out + (int64_t)row * NH * DV;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < HB; ++h)
 #pragma unroll
             for (int j4 = 0; j4 < 4; ++j4) {
                 const f32x4 l4 = *(const f32x4 *)&l_s[h * 32 + 8 * j4 + 4 * half];
@@ -877,8 +577,8 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
 template <int DK, int DV>
 hipError_t launch_dims(const AttnArgs &a, hipStream_t s)
 {
-    if (a.H == 32) attention_kernel<DK, DV, 1><<<dim3((unsigned)a.S), 256, 0, s>>>(a);
-    else if (a.H == 64) attention_split_kernel<DK, DV><<<dim3((unsigned)a.S), 512, 0, s>>>(a);
+    if (a.H == 32) attention_split_kernel<DK, DV, 1><<<dim3((unsigned)a.S), 512, 0, s>>>(a);
+    else if (a.H == 64) attention_split_kernel<DK, DV, 2><<<dim3((unsigned)a.S), 512, 0, s>>>(a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -249,7 +249,8 @@ int csa_profile_collect(double *ms_out, int64_t *launches_out, int32_t n_kinds);
  * dtype must be CSA_BF16 (CSA_F32 gives CSA_ERR_UNSUPPORTED).  This build
  * supports H in {32, 64} and (D_K, D_V) in {(576, 512), (128, 128)}; other
  * positive shapes give CSA_ERR_UNSUPPORTED, as do k > 2^20, S > 2^31 - 1 and
- * T * D_K * 2 >= 2^31.  scale must be finite (else CSA_ERR_BAD_SHAPE).
+ * T * D_K * 2 >= 2^31.  scale must be finite, and so must scale * log2(e)
+ * in fp32, i.e. |scale| below about 2.36e38 (else CSA_ERR_BAD_SHAPE).
  * Enqueued on `stream`; allocates nothing; needs no workspace.
  */
 int csa_sparse_attention(const void *q, const void *kv, const int32_t *idx, void *out,

@@ -278,7 +278,7 @@ __global__ __launch_bounds__(512) void attention_split_kernel(AttnArgs a)
     //   The logit loop is unrolled by three so that every LDS access names its
     // buffer: the compiler then sees that the tile being read is not the one
     // the gather is writing and does not wait for that gather.  The output
-    // loop is not unrolled (unrolled, its 128 accumulators are shuffled
+    // loop is not unrolled (unrolled, its 64*HB accumulators are shuffled
     // between copies and spill); its reads are P and a tile gathered steps
     // earlier, so it picks its buffers at run time.
     int iv0 = -1, iv1 = -1, iv2 = -1;  // idx of tiles 0, 1, 2

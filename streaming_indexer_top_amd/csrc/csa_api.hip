@@ -515,7 +515,9 @@ int csa_sparse_attention(const void *q, const void *kv, const int32_t *idx, void
 {
     if (S < 0 || T < 0 || k < 0 || H <= 0 || D_K <= 0 || D_V <= 0) return CSA_ERR_BAD_SHAPE;
     if (dtype != CSA_BF16) return dtype == CSA_F32 ? CSA_ERR_UNSUPPORTED : CSA_ERR_BAD_DTYPE;
-    if (!std::isfinite(scale)) return CSA_ERR_BAD_SHAPE;
+    // The kernel works with scale * log2(e); it must be finite too.
+    const float scale_log2e = scale * 1.4426950408889634f;
+    if (!std::isfinite(scale) || !std::isfinite(scale_log2e)) return CSA_ERR_BAD_SHAPE;
     if (!csa::attention_shape_supported(H, D_K, D_V)) return CSA_ERR_UNSUPPORTED;
     if (k > ((int64_t)1 << 20) || S > INT32_MAX || T * D_K * 2 >= ((int64_t)1 << 31))
         return CSA_ERR_UNSUPPORTED;
@@ -533,7 +535,7 @@ int csa_sparse_attention(const void *q, const void *kv, const int32_t *idx, void
     a.T = T;
     a.H = H;
     a.k = (int32_t)k;
-    a.scale_log2e = scale * 1.4426950408889634f;
+    a.scale_log2e = scale_log2e;
     hipStream_t s = (hipStream_t)stream;
     return launch_timed(CSA_KERNEL_ATTENTION, s,
                         [&] { return csa::launch_attention(a, D_K, D_V, s); });

@@ -178,6 +178,8 @@ def test_python_binding_rejects_bad_tensors():
     ((4, 10, 0, 576, 512, 8, binding.CSA_BF16, 0.1), 2),
     ((4, 10, 64, 576, 512, 8, binding.CSA_BF16, float("nan")), 2),
     ((4, 10, 64, 576, 512, 8, binding.CSA_BF16, float("inf")), 2),
+    ((4, 10, 64, 576, 512, 8, binding.CSA_BF16, 3.0e38), 2),   # scale * log2(e) overflows fp32
+    ((4, 10, 64, 576, 512, 8, binding.CSA_BF16, -3.0e38), 2),
     ((4, 10, 64, 576, 512, 8, 7, 0.1), 3),
     ((4, 10, 64, 576, 512, 8, binding.CSA_F32, 0.1), 6),
     ((4, 10, 48, 576, 512, 8, binding.CSA_BF16, 0.1), 6),

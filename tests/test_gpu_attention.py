@@ -148,6 +148,39 @@ def test_bench_shape_sampled_rows():
     run_and_check(q, kv, idx, DV, 1.0 / DK ** 0.5, rows=rows)
 
 
+def test_full_composed_shape_sampled_rows():
+    """The page's composed shape for the attention (S = 262,144 query rows,
+    65,536 latent entries, 64 heads, 576/512, k = 2048), in the launch the
+    bench times: one call over every row.  Selections are uniform over the
+    table, with every 97th row padded after 1,500 entries; 24 rows (the
+    first, the last, padded ones and seeded draws) against the oracle.  q
+    (19 GB) and the output (17 GB) are generated and kept on the GPU."""
+    S, T, H, DK, DV, k = 262144, 65536, 64, 576, 512, 2048
+    say("attention full composed shape S=%d T=%d" % (S, T))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    q = torch.empty((S, H, DK), dtype=torch.bfloat16, device=DEV)
+    for r0 in range(0, S, 16384):  # fp32 draws in slices, so the temporary stays small
+        q[r0:r0 + 16384] = torch.randn((16384, H, DK), generator=g, device=DEV).bfloat16()
+    kv = torch.randn((T, DK), generator=g, device=DEV).bfloat16()
+    idx = torch.randint(0, T, (S, k), generator=g, device=DEV, dtype=torch.int32)
+    idx[::97, 1500:] = -1
+    out = csa.sparse_attention(q, kv, idx, DV)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    rows = sorted(set([0, 97, 970, S - 1] + rng.integers(0, S, 20).tolist()))
+    sel = torch.tensor(rows, device=DEV)
+    g_rows = out[sel].float().cpu().numpy()
+    ref, mag = att.sparse_attention_with_magnitude(q[sel].float().cpu().numpy(), kv.float().cpu().numpy(),
+                                                   idx[sel].cpu().numpy(), DV, 1.0 / DK ** 0.5)
+    del q, out
+    torch.cuda.empty_cache()
+    err = np.abs(g_rows - ref)
+    bound = 2.0 ** -8 * (np.abs(ref) + mag) + 1e-6
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, "first failures (sample, head, dim): %s" % bad[:5].tolist()
+
+
 def test_repeat_runs_bit_identical():
     S, T, H, DK, DV, k = 64, 2000, 64, 576, 512, 300
     q, kv = inputs.attention_gaussian(S, T, H, DK, seed=31)

@@ -519,7 +519,9 @@ int csa_sparse_attention(const void *q, const void *kv, const int32_t *idx, void
     const float scale_log2e = scale * 1.4426950408889634f;
     if (!std::isfinite(scale) || !std::isfinite(scale_log2e)) return CSA_ERR_BAD_SHAPE;
     if (!csa::attention_shape_supported(H, D_K, D_V)) return CSA_ERR_UNSUPPORTED;
-    if (k > ((int64_t)1 << 20) || S > INT32_MAX || T * D_K * 2 >= ((int64_t)1 << 31))
+    // T is bounded before the product, so that the product cannot overflow.
+    if (k > ((int64_t)1 << 20) || S > INT32_MAX || T > INT32_MAX ||
+        T * D_K * 2 >= ((int64_t)1 << 31))
         return CSA_ERR_UNSUPPORTED;
     if (S == 0) return CSA_OK;
     if (!q || !out || (k > 0 && !idx) || (T > 0 && !kv)) return CSA_ERR_NULL_PTR;

@@ -186,6 +186,9 @@ def test_python_binding_rejects_bad_tensors():
     ((4, 10, 64, 256, 256, 8, binding.CSA_BF16, 0.1), 6),
     ((4, 10, 64, 576, 512, (1 << 20) + 1, binding.CSA_BF16, 0.1), 6),
     ((4, 1 << 21, 64, 576, 512, 8, binding.CSA_BF16, 0.1), 6),
+    ((4, 1864136, 64, 576, 512, 8, binding.CSA_BF16, 0.1), 6),   # first T with T * 576 * 2 >= 2^31
+    ((4, 1 << 62, 64, 576, 512, 8, binding.CSA_BF16, 0.1), 6),   # T * D_K * 2 would overflow int64
+    ((1 << 31, 10, 64, 576, 512, 8, binding.CSA_BF16, 0.1), 6),
 ])
 def test_sparse_attention_argument_checks(args, status):
     """Bad shapes, dtypes, scales and unsupported sizes are refused before

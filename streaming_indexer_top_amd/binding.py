@@ -121,6 +121,15 @@ def _dtype_code(t: torch.dtype) -> int:
     raise TypeError("q, w, kc must be bfloat16 or float32, got %s" % t)
 
 
+def _caller_buffer(t: torch.Tensor, dev: torch.device, name: str) -> None:
+    """A buffer the caller passes in (outputs, workspace) must be contiguous
+    and on the inputs' GPU: the library gets only its address and size."""
+    if t.device != dev:
+        raise ValueError("%s must be on %s, not %s" % (name, dev, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
 def workspace_size(S, T, H, D, m, k, *, q_pos0=0, dtype=torch.bfloat16, chunk_keys=0,
                    key_tile=0, workspace_budget=0, key_splits=0) -> int:
     out = ctypes.c_size_t(0)
@@ -181,16 +190,18 @@ def topk(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: int, *,
     else:
         idx, score = out
         if tuple(idx.shape) != oshape or tuple(score.shape) != oshape \
-                or idx.dtype != torch.int32 or score.dtype != torch.float32 \
-                or not idx.is_contiguous() or not score.is_contiguous():
+                or idx.dtype != torch.int32 or score.dtype != torch.float32:
             raise ValueError("out must be contiguous int32/float32 tensors of shape %s"
                              % (oshape,))
+        _caller_buffer(idx, dev, "out idx")
+        _caller_buffer(score, dev, "out score")
     if workspace is None:
         nbytes = workspace_size(S, T, H, D, m, k, q_pos0=q_pos0, dtype=q.dtype,
                                 chunk_keys=chunk_keys, key_tile=key_tile,
                                 workspace_budget=workspace_budget, key_splits=key_splits)
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
     else:
+        _caller_buffer(workspace, dev, "workspace")
         nbytes = workspace.numel() * workspace.element_size()
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
@@ -240,10 +251,11 @@ def topk_noalloc(q: torch.Tensor, w: torch.Tensor, kc: torch.Tensor, m: int, k: 
     else:
         idx, score = out
         if tuple(idx.shape) != (S, k) or tuple(score.shape) != (S, k) \
-                or idx.dtype != torch.int32 or score.dtype != torch.float32 \
-                or not idx.is_contiguous() or not score.is_contiguous():
+                or idx.dtype != torch.int32 or score.dtype != torch.float32:
             raise ValueError("out must be contiguous int32/float32 tensors of shape %s"
                              % ((S, k),))
+        _caller_buffer(idx, dev, "out idx")
+        _caller_buffer(score, dev, "out score")
     o = _opts(chunk_keys, key_tile, workspace_budget, key_splits)
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):
@@ -286,8 +298,10 @@ def sparse_attention(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, d_v: 
     oshape = (S, H, int(d_v))
     if out is None:
         out = torch.empty(oshape, dtype=torch.bfloat16, device=dev)
-    elif tuple(out.shape) != oshape or out.dtype != torch.bfloat16 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor of shape %s" % (oshape,))
+    else:
+        if tuple(out.shape) != oshape or out.dtype != torch.bfloat16:
+            raise ValueError("out must be a contiguous bfloat16 tensor of shape %s" % (oshape,))
+        _caller_buffer(out, dev, "out")
     lib = load_library()
     stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):

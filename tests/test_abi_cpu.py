@@ -171,6 +171,20 @@ def test_python_binding_rejects_bad_tensors():
         csa.topk(q, w[:3], kc, 4, 2)
 
 
+def test_caller_buffers_must_be_contiguous_and_on_the_inputs_device():
+    # Outputs and workspace that the caller passes in reach the library only
+    # as an address and a size, so the binding checks where they live.
+    cpu = torch.device("cpu")
+    binding._caller_buffer(torch.zeros(4), cpu, "out")
+    with pytest.raises(ValueError, match="must be on"):
+        binding._caller_buffer(torch.zeros(4), torch.device("cuda", 0), "out")
+    with pytest.raises(ValueError, match="contiguous"):
+        binding._caller_buffer(torch.zeros(4, 4).t(), cpu, "out")
+    # A stride-0 view reports far more bytes than it holds.
+    with pytest.raises(ValueError, match="contiguous"):
+        binding._caller_buffer(torch.zeros(1, dtype=torch.uint8).expand(1 << 20), cpu, "workspace")
+
+
 @pytest.mark.parametrize("args, status", [
     # (S, T, H, D_K, D_V, k, dtype, scale)
     ((-1, 10, 64, 576, 512, 8, binding.CSA_BF16, 0.1), 2),

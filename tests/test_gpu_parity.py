@@ -575,3 +575,27 @@ def test_full_size_chunk_and_tile_grid_integer_bit_exact():
         idx, sc = csa.topk(qd, wd, kd, m, k, q_pos0=q_pos0, **kw)
         torch.cuda.synchronize()
         assert_no_fail(checks.check_exact(idx.cpu().numpy(), sc.cpu().numpy(), o_idx, o_sc))
+
+
+def test_host_or_strided_caller_buffers_are_refused():
+    """Outputs or a workspace in host memory, or a stride-0 workspace, are
+    refused by the binding before any library call."""
+    say("caller buffers on the host")
+    q, w, kc = inputs.integer_valued(64, 16, 4, 32, seed=3, dtype=torch.bfloat16)
+    q, w, kc = q.to(DEV), w.to(DEV), kc.to(DEV)
+    host_out = (torch.empty((64, 8), dtype=torch.int32), torch.empty((64, 8), dtype=torch.float32))
+    with pytest.raises(ValueError, match="must be on"):
+        csa.topk(q, w, kc, 4, 8, out=host_out)
+    with pytest.raises(ValueError, match="must be on"):
+        csa.topk_noalloc(q, w, kc, 4, 8, out=host_out)
+    with pytest.raises(ValueError, match="must be on"):
+        csa.topk(q, w, kc, 4, 8, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="contiguous"):
+        csa.topk(q, w, kc, 4, 8,
+                 workspace=torch.zeros(1, dtype=torch.uint8, device=DEV).expand(1 << 24))
+    qa = torch.zeros((4, 64, 128), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((16, 128), dtype=torch.bfloat16, device=DEV)
+    ia = torch.zeros((4, 8), dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError, match="must be on"):
+        csa.sparse_attention(qa, kv, ia, 128, out=torch.empty((4, 64, 128), dtype=torch.bfloat16))
+    torch.cuda.synchronize()

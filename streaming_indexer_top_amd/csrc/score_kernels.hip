@@ -466,8 +466,11 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     }
 }
 
-// fp32 path: one workgroup per (row, 256-key block); one thread per key.
-// The head dimension loop is plain fp32 FMA.
+// fp32 path: one workgroup per (row, block of kF32Keys keys), which loads
+// the row's q into LDS once and gives each thread every 256th key of the
+// block, held in registers.  The head-dimension loop is plain fp32 FMA with
+// q read from LDS by broadcast.
+constexpr int kF32Keys = 1024;
 template <int D>
 __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a)
 {
@@ -478,27 +481,27 @@ __global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a)
     const int64_t row = a.row0 + rl;
     const int64_t n = n_usable(a.q_pos0 + row, a.T, a.m);
     const int64_t kend = min(a.c0 + a.clen, n);
-    const int64_t k0 = a.c0 + (int64_t)blockIdx.y * 256;
+    const int64_t k0 = a.c0 + (int64_t)blockIdx.y * kF32Keys;
     if (k0 >= kend) return;
     const int H = a.H;
     const float *qrow = (const float *)a.q + row * (int64_t)H * D;
     for (int e = tid; e < H * D; e += 256) qs[e] = qrow[e];
     for (int e = tid; e < H; e += 256) wsh[e] = ((const float *)a.w)[row * H + e];
     __syncthreads();
-    const int64_t gk = k0 + tid;
-    if (gk >= kend) return;
-    const float *key = (const float *)a.kc + gk * D;
-    float kr[D];
+    for (int64_t gk = k0 + tid; gk < min(kend, k0 + kF32Keys); gk += 256) {
+        const float *key = (const float *)a.kc + gk * D;
+        float kr[D];
 #pragma unroll
-    for (int d = 0; d < D; ++d) kr[d] = key[d];
-    float s = 0.0f;
-    for (int h = 0; h < H; ++h) {
-        float acc = 0.0f;
+        for (int d = 0; d < D; ++d) kr[d] = key[d];
+        float s = 0.0f;
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc = fmaf(qs[h * D + d], kr[d], acc);
-        s = fmaf(wsh[h], fmaxf(acc, 0.0f), s);
+            for (int d = 0; d < D; ++d) acc = fmaf(qs[h * D + d], kr[d], acc);
+            s = fmaf(wsh[h], fmaxf(acc, 0.0f), s);
+        }
+        a.ws[rl * a.clen + (gk - a.c0)] = orderable(s);
     }
-    a.ws[rl * a.clen + (gk - a.c0)] = orderable(s);
 }
 
 template <int D, int HT, int NT, bool DB, int WAVES>
@@ -599,7 +602,7 @@ hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t ke
         default: return hipErrorInvalidValue;
         }
     }
-    dim3 grid((unsigned)a.rows, (unsigned)((a.clen + 255) / 256));
+    dim3 grid((unsigned)a.rows, (unsigned)((a.clen + kF32Keys - 1) / kF32Keys));
     switch (D) {
     case 32: score_f32_kernel<32><<<grid, 256, 0, stream>>>(a); break;
     case 64: score_f32_kernel<64><<<grid, 256, 0, stream>>>(a); break;

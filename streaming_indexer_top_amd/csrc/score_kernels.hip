@@ -25,7 +25,8 @@
 // chunk's keys (few query rows, e.g. decoding); the kernel details are at
 // score_bf16_kernel below.
 //
-// fp32 path: one thread per key, plain fp32 FMA (correctness path).
+// fp32 path: the same contraction on v_mfma_f32_32x32x2_f32, with q resident
+// in registers and 32-key tiles staged in LDS (score_f32_kernel below).
 #include "csa_internal.h"
 
 namespace csa {
@@ -466,41 +467,134 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     }
 }
 
-// fp32 path: one workgroup per (row, block of kF32Keys keys), which loads
-// the row's q into LDS once and gives each thread every 256th key of the
-// block, held in registers.  The head-dimension loop is plain fp32 FMA with
-// q read from LDS by broadcast.
+// fp32 path on the matrix cores: v_mfma_f32_32x32x2_f32 (the fp32 matrix
+// rate equals the fp32 vector peak, and the products leave the VALU free).
+// Workgroup: 8 waves, one query row each, over kF32Keys keys of the chunk
+// (heaviest rows first).  A = q, 32 heads x 2 dims per MFMA, resident in
+// registers for the whole workgroup; B = kc, 2 dims x 32 keys, from a
+// 32-key LDS tile that all waves stage together, double-buffered behind one
+// barrier per tile.  k-step s covers dims 2s (lanes 0-31) and 2s+1 (lanes
+// 32-63); each key's LDS row holds its even dims, then its odd dims, so one
+// 16-byte read gives a lane four consecutive k-steps.  The accumulator layout
+// is that of the bf16 kernel: lane l owns key l%32 and 16 of each 32-head
+// block's rows, so ReLU and the weighted head sum run in registers and one
+// 32-lane swap adds the two half-waves' shares.
 constexpr int kF32Keys = 1024;
-template <int D>
-__global__ __launch_bounds__(256) void score_f32_kernel(ScoreArgs a)
+template <int D, int HT>
+__global__ __launch_bounds__(512) void score_f32_kernel(ScoreArgs a)
 {
-    __shared__ float qs[64 * D];
-    __shared__ float wsh[64];
+    constexpr int KS = D / 2;        // k-steps
+    constexpr int ROW = D + 4;       // LDS floats per key row (padded against bank conflicts)
+    constexpr int TILE = 32 * ROW;   // LDS floats per 32-key tile
+    constexpr int F4 = 8 * D;        // 16-byte pieces of a tile in global memory
+    constexpr int PER = (F4 + 511) / 512;
+    __shared__ __attribute__((aligned(16))) float tile[2][TILE];
     const int tid = threadIdx.x;
-    const int64_t rl = (int64_t)blockIdx.x;
-    const int64_t row = a.row0 + rl;
-    const int64_t n = n_usable(a.q_pos0 + row, a.T, a.m);
-    const int64_t kend = min(a.c0 + a.clen, n);
-    const int64_t k0 = a.c0 + (int64_t)blockIdx.y * kF32Keys;
-    if (k0 >= kend) return;
-    const int H = a.H;
-    const float *qrow = (const float *)a.q + row * (int64_t)H * D;
-    for (int e = tid; e < H * D; e += 256) qs[e] = qrow[e];
-    for (int e = tid; e < H; e += 256) wsh[e] = ((const float *)a.w)[row * H + e];
-    __syncthreads();
-    for (int64_t gk = k0 + tid; gk < min(kend, k0 + kF32Keys); gk += 256) {
-        const float *key = (const float *)a.kc + gk * D;
-        float kr[D];
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int c = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    const int64_t nqb = (a.rows + 7) / 8;
+    const int64_t qb = nqb - 1 - (int64_t)blockIdx.x;
+    const int64_t rl = qb * 8 + wave;
+    const bool active = rl < a.rows;
+    const int64_t last = min(qb * 8 + 7, a.rows - 1);
+    const int64_t n_hi = n_usable(a.q_pos0 + a.row0 + last, a.T, a.m);
+    const int64_t kb0 = a.c0 + (int64_t)blockIdx.y * kF32Keys;
+    const int64_t k_end = min(min(a.c0 + a.clen, kb0 + kF32Keys), n_hi);
+    if (kb0 >= k_end) return;  // uniform: no row of this block has a key here
+    const int64_t my_end =
+        active ? min(k_end, n_usable(a.q_pos0 + a.row0 + rl, a.T, a.m)) : kb0;
+
+    // Resident A operand and the weights of this lane's accumulator rows
+    // (heads past H, and inactive rows, are zero).
+    float qa[HT][KS];
+    float wv[HT][16];
+    {
+        const int64_t row = a.row0 + (active ? rl : 0);
+        const float *qrow = (const float *)a.q + row * (int64_t)a.H * D;
+        const float *wrow = (const float *)a.w + row * (int64_t)a.H;
 #pragma unroll
-        for (int d = 0; d < D; ++d) kr[d] = key[d];
-        float s = 0.0f;
-        for (int h = 0; h < H; ++h) {
-            float acc = 0.0f;
+        for (int ht = 0; ht < HT; ++ht) {
+            const int h = min(ht * 32 + c, a.H - 1);
+            const bool hv = active && ht * 32 + c < a.H;
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc = fmaf(qs[h * D + d], kr[d], acc);
-            s = fmaf(wsh[h], fmaxf(acc, 0.0f), s);
+            for (int i = 0; i < D / 4; ++i) {
+                const float4 x = *(const float4 *)(qrow + (int64_t)h * D + 4 * i);
+                qa[ht][2 * i] = hv ? (half ? x.y : x.x) : 0.0f;      // dim 4i + half
+                qa[ht][2 * i + 1] = hv ? (half ? x.w : x.z) : 0.0f;  // dim 4i + 2 + half
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int hr = ht * 32 + ((r >> 2) << 3) + (half << 2) + (r & 3);
+                wv[ht][r] = (active && hr < a.H) ? wrow[min(hr, a.H - 1)] : 0.0f;
+            }
         }
-        a.ws[rl * a.clen + (gk - a.c0)] = orderable(s);
+    }
+
+    // Tile staging: piece f = key * D/4 + i holds dims 4i..4i+3 of the key;
+    // its even dims go to row positions 2i, 2i+1 and its odd dims to KS + 2i,
+    // KS + 2i + 1.  Keys past k_end read the last usable key (never stored).
+    float4 st[PER];
+    auto gload = [&](int t) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int f = p * 512 + tid;
+            if (f < F4) {
+                const int64_t key = min(kb0 + (int64_t)t * 32 + f / (D / 4), k_end - 1);
+                st[p] = *(const float4 *)((const float *)a.kc + key * D + 4 * (f % (D / 4)));
+            }
+        }
+    };
+    auto lstore = [&](float *dst) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int f = p * 512 + tid;
+            if (f < F4) {
+                float *r = dst + (f / (D / 4)) * ROW + 2 * (f % (D / 4));
+                *(float2 *)r = make_float2(st[p].x, st[p].z);
+                *(float2 *)(r + KS) = make_float2(st[p].y, st[p].w);
+            }
+        }
+    };
+
+    uint32_t *wsrow = a.ws + (active ? rl : 0) * a.clen;
+    const int nblk = (int)((k_end - kb0 + 31) / 32);
+    gload(0);
+    lstore(tile[0]);
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk + 1 < nblk) gload(blk + 1);
+        const float *tb = tile[blk & 1] + c * ROW + half * KS;
+        f32x16 acc[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x16{};
+#pragma unroll
+        for (int j = 0; j < KS / 4; ++j) {
+            const float4 b = *(const float4 *)(tb + 4 * j);
+            const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+                    acc[ht] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[ht][4 * j + t], bv[t], acc[ht],
+                                                                   0, 0, 0);
+        }
+        // This lane's share of key c's score (its 16 rows of each head
+        // block), then the other half-wave's share.
+        float part = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.0f), part);
+        const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
+                                                        false, false);
+        const float sc = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+        const int64_t key = kb0 + (int64_t)blk * 32 + c;
+        if (half == 0 && key < my_end) wsrow[key - a.c0] = orderable(sc);
+        if (blk + 1 < nblk) lstore(tile[(blk + 1) & 1]);
+        __syncthreads();
     }
 }
 
@@ -602,11 +696,21 @@ hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t ke
         default: return hipErrorInvalidValue;
         }
     }
-    dim3 grid((unsigned)a.rows, (unsigned)((a.clen + kF32Keys - 1) / kF32Keys));
+    dim3 grid((unsigned)((a.rows + 7) / 8), (unsigned)((a.clen + kF32Keys - 1) / kF32Keys));
+    const bool two = a.H > 32;
     switch (D) {
-    case 32: score_f32_kernel<32><<<grid, 256, 0, stream>>>(a); break;
-    case 64: score_f32_kernel<64><<<grid, 256, 0, stream>>>(a); break;
-    case 128: score_f32_kernel<128><<<grid, 256, 0, stream>>>(a); break;
+    case 32:
+        if (two) score_f32_kernel<32, 2><<<grid, 512, 0, stream>>>(a);
+        else score_f32_kernel<32, 1><<<grid, 512, 0, stream>>>(a);
+        break;
+    case 64:
+        if (two) score_f32_kernel<64, 2><<<grid, 512, 0, stream>>>(a);
+        else score_f32_kernel<64, 1><<<grid, 512, 0, stream>>>(a);
+        break;
+    case 128:
+        if (two) score_f32_kernel<128, 2><<<grid, 512, 0, stream>>>(a);
+        else score_f32_kernel<128, 1><<<grid, 512, 0, stream>>>(a);
+        break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

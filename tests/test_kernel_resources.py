@@ -65,10 +65,20 @@ def test_score_kernels_no_scratch_and_two_waves_per_simd(score_asm):
     for name, m in bf16.items():
         assert m["vgpr_spill_count"] == 0, name
         assert m["private_segment_fixed_size"] == 0, name
-    # The bench configuration (D_I=128, 64 heads, 128-key tiles): two waves
-    # per SIMD, i.e. at most 256 registers.
-    main = "_ZN3csa12_GLOBAL__N_117score_bf16_kernelILi128ELi2ELi128ELb1ELi8EEEvNS_9ScoreArgsE"
-    assert bf16[main]["vgpr_count"] <= 256
+    # D_I=128 with 64 heads and double-buffered 128- or 192-key tiles (the
+    # latter is the automatic choice): two waves per SIMD, i.e. at most 256
+    # registers.
+    for tile in (128, 192):
+        main = ("_ZN3csa12_GLOBAL__N_117score_bf16_kernelILi128ELi2ELi%dELb1ELi8EEEvNS_9ScoreArgsE"
+                % tile)
+        assert bf16[main]["vgpr_count"] <= 256, main
+    # The fp32 path keeps q for up to 64 heads resident (128 registers at
+    # D_I=128) in 8-wave workgroups: no spills, at most 256 registers.
+    f32 = {n: m for n, m in meta.items() if "score_f32_kernel" in n}
+    assert len(f32) == 6
+    for name, m in f32.items():
+        assert m["vgpr_spill_count"] == 0 and m["private_segment_fixed_size"] == 0, name
+        assert m["vgpr_count"] <= 256, name
 
 
 def test_select_kernels_no_scratch_on_the_hot_path(select_asm):

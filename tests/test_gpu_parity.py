@@ -92,6 +92,34 @@ EDGE_CASES = [
 ]
 
 
+@pytest.mark.parametrize("chunk", [0, 1280])
+def test_fp32_several_key_blocks_bit_exact(chunk):
+    """fp32 integer inputs whose rows see about 3,250-3,300 keys: each row's
+    chunk spans several 1,024-key workgroups of the fp32 kernel with a ragged
+    last one, the last query block is ragged (203 rows), and with 1,280-key
+    chunks the running lists are merged across three chunks."""
+    S, T, H, D, m, k, q_pos0 = 203, 3500, 64, 128, 4, 300, 13000
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=77, dtype=torch.float32, signed_w=True)
+    say("fp32 several key blocks chunk=%d" % chunk)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, chunk_keys=chunk)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
+def test_fp32_gaussian_several_key_blocks():
+    """fp32 Gaussian inputs, 1,024 rows that see about 2,000-2,250 keys each
+    (three 1,024-key workgroups per row), by the tolerance rules."""
+    S, T, H, D, m, k, q_pos0 = 1024, 4096, 64, 128, 4, 512, 8000
+    q, w, kc = inputs.gaussian_fp32(S, T, H, D, seed=5)
+    say("fp32 gaussian several key blocks")
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    fails, stats = checks.check_float(g_idx, g_sc, o_idx, o_sc, q.numpy(), w.numpy(),
+                                      kc.numpy(), np.arange(S) + q_pos0, T, m, k)
+    say("stats %s" % stats)
+    assert_no_fail(fails)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("case", EDGE_CASES)
 def test_edge_cases_bit_exact(dtype, case):

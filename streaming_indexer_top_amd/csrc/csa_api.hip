@@ -253,7 +253,7 @@ const char *csa_status_str(int status)
     case CSA_ERR_BAD_DTYPE: return "bad dtype: expected CSA_F32 or CSA_BF16";
     case CSA_ERR_MISALIGNED: return "misaligned pointer";
     case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small for one query block";
-    case CSA_ERR_UNSUPPORTED: return "unsupported request (k > 4096 or T >= 2^31)";
+    case CSA_ERR_UNSUPPORTED: return "unsupported request: indexer k > 4096 or T >= 2^31; attention dtype, shape or size outside this build";
     case CSA_ERR_HIP: return "HIP call or kernel launch failed";
     case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256 up to 2^24, key_tile one of 64/128/192/256, key_splits 0 or a power of two up to 64, reserved fields 0";
     case CSA_ERR_SCRATCH_TOO_SMALL: return "allocation-free call: one query block needs more scratch than the library's fixed 256 MiB (use a smaller chunk_keys, or csa_indexer_topk with a workspace)";

@@ -89,10 +89,10 @@ typedef struct csa_opts {
      * and merges them into a running list.  A multiple of 256 up to 2^24, or
      * 0. */
     int64_t chunk_keys;
-    /* Keys staged in LDS per step of the score kernel: 64, 128, 192, 256, or
-     * 0 (automatic: 192). */
+    /* Keys staged in LDS per step of the bf16 score kernel: 64, 128, 192,
+     * 256, or 0 (automatic: 192).  The fp32 path always stages 32 keys. */
     int32_t key_tile;
-    /* Key splits (bf16 only, ignored when chunk_keys is set): the usable keys
+    /* Key splits (ignored when chunk_keys is set): the usable keys
      * form one chunk cut into this many splits that are scored and selected
      * in parallel, each split's best k going to its own list, and the lists
      * are merged in rounds that combine four lists (k <= 2048) or two.

@@ -148,10 +148,9 @@ Plan make_plan(int64_t S, int64_t T, int32_t m, int64_t q_pos0, int64_t k, int32
     const int64_t n_round = (p.n_max + 255) / 256 * 256;
     const bool user_chunk = opts && opts->chunk_keys;
     const int32_t ks = opts ? opts->key_splits : 0;
-    // Key splits: bf16 only (the fp32 path has no chunk summaries), not with
-    // a chunk size the caller fixed.
+    // Key splits: not with a chunk size the caller fixed.
     int64_t g = 1;
-    if (dtype == CSA_BF16 && !user_chunk && ks != 1) {
+    if (!user_chunk && ks != 1) {
         if (ks >= 2) {
             g = ks;
         } else {
@@ -322,9 +321,9 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
             // Several passes.  Score workgroups of one pass run in rounds of
             // (CUs x workgroups per CU); a partial round leaves CUs idle for
             // a whole workgroup's time, so passes get whole rounds (only the
-            // last pass has a partial one).  Without a round size (fp32, or
-            // the queries fail), rows are spread evenly over the passes so
-            // that no pass is a handful of rows on a handful of CUs.
+            // last pass has a partial one).  Without a round size (the
+            // queries fail), rows are spread evenly over the passes so that
+            // no pass is a handful of rows on a handful of CUs.
             int dev = 0, ncu = 0;
             int64_t round_rows = 0;
             if (hipGetDevice(&dev) == hipSuccess &&
@@ -388,7 +387,7 @@ int run_call(const void *q, const void *w, const void *kc, int32_t dtype, int64_
             }
             csa::SelectArgs se;
             se.ws = ws_scores;
-            se.meta = dtype == CSA_BF16 ? meta : nullptr;
+            se.meta = meta;
             se.lists = lists;
             se.state = state;
             se.out_idx = idx;

@@ -107,14 +107,14 @@ struct MergeArgs {
 // Dtype codes as in the public header.
 enum { DT_F32 = 0, DT_BF16 = 1 };
 
-// Score kernel: grid ceil(rows/8) x splits workgroups for bf16 (each covers
-// its split of the chunk for its 8 rows; the chunk summary of row r in split
-// y goes to meta[y*rows + r]) or (rows x ceil(clen/256)) for fp32 (no splits).
+// Score kernel (either dtype): grid ceil(rows/8) x splits workgroups, each
+// covering its split of the chunk for its 8 rows; the chunk summary of row r
+// in split y goes to meta[y*rows + r].  key_tile applies to bf16 only.
 hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t key_tile,
                         hipStream_t stream);
 
-// Score workgroups that one CU runs at once (bf16 path; 0 for fp32 or on
-// error), for sizing passes in whole rounds of workgroups.
+// Score workgroups that one CU runs at once (0 on error), for sizing passes
+// in whole rounds of workgroups.
 int score_blocks_per_cu(int32_t dtype, int32_t D, int32_t H, int32_t key_tile);
 
 // Select kernel: one workgroup per (virtual) row of the batch.

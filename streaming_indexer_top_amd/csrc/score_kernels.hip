@@ -74,6 +74,50 @@ __device__ inline float relu_bits(float x)
     return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// Chunk summary of one wave's row histogram h (kHistBins counts over the
+// top bits of the orderable scores of the keys it counted): the bin b* that
+// holds the need-th best counted key, the counts above b* and in it, and the
+// total counted (with total <= need only the total matters).  One lane of
+// the wave writes *dst.
+__device__ __forceinline__ void write_chunk_summary(const uint32_t *h, int lane, uint32_t need,
+                                                    ChunkMeta *dst)
+{
+    constexpr int PERL = kHistBins / 64;
+    uint32_t mine = 0;
+#pragma unroll 8
+    for (int i = 0; i < PERL; ++i) mine += h[lane * PERL + i];
+    uint32_t incl = mine;  // sum over lanes >= this lane
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(incl, off);
+        if (lane + off < 64) incl += y;
+    }
+    const uint32_t total = __shfl(incl, 0);
+    ChunkMeta m = {0u, 0u, 0u, total};
+    if (total > need) {
+        const uint32_t above_lane = incl - mine;
+        const bool here = above_lane < need && need <= incl;
+        const uint64_t who = __ballot(here);
+        const int src = __builtin_ctzll(who);
+        if (lane == src) {
+            uint32_t above = above_lane;
+            for (int i = PERL - 1; i >= 0; --i) {
+                const uint32_t c = h[lane * PERL + i];
+                if (above + c >= need) {
+                    m.bin = (uint32_t)(lane * PERL + i);
+                    m.above = above;
+                    m.in_bin = c;
+                    break;
+                }
+                above += c;
+            }
+            *dst = m;
+        }
+    } else if (lane == 0) {
+        *dst = m;
+    }
+}
+
 // D: head dimension; HT: 32-head blocks (ceil(H/32), at most 2); NT: keys
 // per LDS tile; DB: double-buffered tiles.  Block = 8 waves, one query row
 // each, covering the whole chunk for its rows.  Grid: query blocks of the
@@ -428,58 +472,23 @@ __global__ __launch_bounds__(WAVES * 64) void score_bf16_kernel(ScoreArgs a)
     if (pend) flush();
 
     // Chunk summary: locate the bin that holds the k-th best counted key.
-    if (active && a.meta) {
-        constexpr int PERL = kHistBins / 64;
-        uint32_t mine = 0;
-#pragma unroll 8
-        for (int i = 0; i < PERL; ++i) mine += h[lane * PERL + i];
-        uint32_t incl = mine;  // sum over lanes >= this lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_down(incl, off);
-            if (lane + off < 64) incl += y;
-        }
-        const uint32_t total = __shfl(incl, 0);
-        const uint32_t need = (uint32_t)a.k;
-        ChunkMeta m = {0u, 0u, 0u, total};
-        if (total > need) {
-            const uint32_t above_lane = incl - mine;
-            const bool here = above_lane < need && need <= incl;
-            const uint64_t who = __ballot(here);
-            const int src = __builtin_ctzll(who);
-            if (lane == src) {
-                uint32_t above = above_lane;
-                for (int i = PERL - 1; i >= 0; --i) {
-                    const uint32_t c = h[lane * PERL + i];
-                    if (above + c >= need) {
-                        m.bin = (uint32_t)(lane * PERL + i);
-                        m.above = above;
-                        m.in_bin = c;
-                        break;
-                    }
-                    above += c;
-                }
-                a.meta[split * a.rows + rl] = m;
-            }
-        } else if (lane == 0) {
-            a.meta[split * a.rows + rl] = m;
-        }
-    }
+    if (active && a.meta) write_chunk_summary(h, lane, (uint32_t)a.k, a.meta + split * a.rows + rl);
 }
 
 // fp32 path on the matrix cores: v_mfma_f32_32x32x2_f32 (the fp32 matrix
 // rate equals the fp32 vector peak, and the products leave the VALU free).
-// Workgroup: 8 waves, one query row each, over kF32Keys keys of the chunk
-// (heaviest rows first).  A = q, 32 heads x 2 dims per MFMA, resident in
-// registers for the whole workgroup; B = kc, 2 dims x 32 keys, from a
-// 32-key LDS tile that all waves stage together, double-buffered behind one
-// barrier per tile.  k-step s covers dims 2s (lanes 0-31) and 2s+1 (lanes
-// 32-63); each key's LDS row holds its even dims, then its odd dims, so one
-// 16-byte read gives a lane four consecutive k-steps.  The accumulator layout
-// is that of the bf16 kernel: lane l owns key l%32 and 16 of each 32-head
-// block's rows, so ReLU and the weighted head sum run in registers and one
-// 32-lane swap adds the two half-waves' shares.
-constexpr int kF32Keys = 1024;
+// Workgroup: 8 waves, one query row each, over the keys of one chunk (or of
+// one split of it, blockIdx.y), heaviest rows first, as in the bf16 kernel.
+// A = q, 32 heads x 2 dims per MFMA, resident in registers for the whole
+// workgroup; B = kc, 2 dims x 32 keys, from a 32-key LDS tile that all
+// waves stage together, double-buffered behind one barrier per tile.
+// k-step s covers dims 2s (lanes 0-31) and 2s+1 (lanes 32-63); each key's
+// LDS row holds its even dims, then its odd dims, so one 16-byte read gives
+// a lane four consecutive k-steps.  The accumulator layout is that of the
+// bf16 kernel: lane l owns key l%32 and 16 of each 32-head block's rows, so
+// ReLU and the weighted head sum run in registers and one 32-lane swap adds
+// the two half-waves' shares.  Each wave also builds its row's histogram
+// and chunk summary exactly as the bf16 kernel does.
 template <int D, int HT>
 __global__ __launch_bounds__(512) void score_f32_kernel(ScoreArgs a)
 {
@@ -489,6 +498,7 @@ __global__ __launch_bounds__(512) void score_f32_kernel(ScoreArgs a)
     constexpr int F4 = 8 * D;        // 16-byte pieces of a tile in global memory
     constexpr int PER = (F4 + 511) / 512;
     __shared__ __attribute__((aligned(16))) float tile[2][TILE];
+    __shared__ uint32_t hist_all[8 * kHistBins];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int half = lane >> 5;
@@ -501,11 +511,25 @@ __global__ __launch_bounds__(512) void score_f32_kernel(ScoreArgs a)
     const bool active = rl < a.rows;
     const int64_t last = min(qb * 8 + 7, a.rows - 1);
     const int64_t n_hi = n_usable(a.q_pos0 + a.row0 + last, a.T, a.m);
-    const int64_t kb0 = a.c0 + (int64_t)blockIdx.y * kF32Keys;
-    const int64_t k_end = min(min(a.c0 + a.clen, kb0 + kF32Keys), n_hi);
+    const int64_t split = (int64_t)blockIdx.y;
+    const int64_t kb0 = a.c0 + split * a.slen;
+    const int64_t kcap = min(a.c0 + a.clen, kb0 + a.slen);
+    const int64_t k_end = min(kcap, n_hi);
     if (kb0 >= k_end) return;  // uniform: no row of this block has a key here
     const int64_t my_end =
-        active ? min(k_end, n_usable(a.q_pos0 + a.row0 + rl, a.T, a.m)) : kb0;
+        active ? min(kcap, n_usable(a.q_pos0 + a.row0 + rl, a.T, a.m)) : kb0;
+
+    // Keys must beat the row's running k-th key to be counted (chunk keys
+    // come after every key already in the list, so equal scores lose).
+    uint32_t u_floor = 0;
+    bool filt = false;
+    if (active && a.state) {
+        const uint64_t th = a.state[rl].theta;
+        filt = th != 0;
+        u_floor = (uint32_t)(th >> 32);
+    }
+    for (int e = tid; e < 8 * kHistBins; e += 512) hist_all[e] = 0u;
+    uint32_t *h = hist_all + wave * kHistBins;
 
     // Resident A operand and the weights of this lane's accumulator rows
     // (heads past H, and inactive rows, are zero).
@@ -517,11 +541,11 @@ __global__ __launch_bounds__(512) void score_f32_kernel(ScoreArgs a)
         const float *wrow = (const float *)a.w + row * (int64_t)a.H;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            const int h = min(ht * 32 + c, a.H - 1);
+            const int hq = min(ht * 32 + c, a.H - 1);
             const bool hv = active && ht * 32 + c < a.H;
 #pragma unroll
             for (int i = 0; i < D / 4; ++i) {
-                const float4 x = *(const float4 *)(qrow + (int64_t)h * D + 4 * i);
+                const float4 x = *(const float4 *)(qrow + (int64_t)hq * D + 4 * i);
                 qa[ht][2 * i] = hv ? (half ? x.y : x.x) : 0.0f;      // dim 4i + half
                 qa[ht][2 * i + 1] = hv ? (half ? x.w : x.z) : 0.0f;  // dim 4i + 2 + half
             }
@@ -563,7 +587,7 @@ __global__ __launch_bounds__(512) void score_f32_kernel(ScoreArgs a)
     const int nblk = (int)((k_end - kb0 + 31) / 32);
     gload(0);
     lstore(tile[0]);
-    __syncthreads();
+    __syncthreads();  // also orders the histogram clear before any count
     for (int blk = 0; blk < nblk; ++blk) {
         if (blk + 1 < nblk) gload(blk + 1);
         const float *tb = tile[blk & 1] + c * ROW + half * KS;
@@ -590,12 +614,18 @@ __global__ __launch_bounds__(512) void score_f32_kernel(ScoreArgs a)
             for (int r = 0; r < 16; ++r) part = fmaf(wv[ht][r], fmaxf(acc[ht][r], 0.0f), part);
         const auto z = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part),
                                                         false, false);
-        const float sc = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+        const uint32_t u = orderable(__uint_as_float(z[0]) + __uint_as_float(z[1]));
         const int64_t key = kb0 + (int64_t)blk * 32 + c;
-        if (half == 0 && key < my_end) wsrow[key - a.c0] = orderable(sc);
+        if (half == 0 && key < my_end) {
+            wsrow[key - a.c0] = u;
+            if (!filt || u > u_floor) atomicAdd(&h[u >> (32 - kHistBits)], 1u);
+        }
         if (blk + 1 < nblk) lstore(tile[(blk + 1) & 1]);
         __syncthreads();
     }
+
+    // Chunk summary: locate the bin that holds the k-th best counted key.
+    if (active && a.meta) write_chunk_summary(h, lane, (uint32_t)a.k, a.meta + split * a.rows + rl);
 }
 
 template <int D, int HT, int NT, bool DB, int WAVES>
@@ -669,12 +699,29 @@ hipError_t launch_bf16_d(const ScoreArgs &a, int32_t key_tile, hipStream_t s)
     return launch_bf16_tile<D, 2>(a, key_tile, s);
 }
 
+template <int D, int HT>
+int blocks_per_cu_f32()
+{
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, (const void *)score_f32_kernel<D, HT>, 512,
+                                                     0) != hipSuccess)
+        return 0;
+    return n;
+}
+
 }  // namespace
 
 int score_blocks_per_cu(int32_t dtype, int32_t D, int32_t H, int32_t key_tile)
 {
-    if (dtype != DT_BF16) return 0;
     const bool two = H > 32;
+    if (dtype != DT_BF16) {
+        switch (D) {
+        case 32: return two ? blocks_per_cu_f32<32, 2>() : blocks_per_cu_f32<32, 1>();
+        case 64: return two ? blocks_per_cu_f32<64, 2>() : blocks_per_cu_f32<64, 1>();
+        case 128: return two ? blocks_per_cu_f32<128, 2>() : blocks_per_cu_f32<128, 1>();
+        default: return 0;
+        }
+    }
     switch (D) {
     case 32: return two ? blocks_per_cu_tile<32, 2>(key_tile) : blocks_per_cu_tile<32, 1>(key_tile);
     case 64: return two ? blocks_per_cu_tile<64, 2>(key_tile) : blocks_per_cu_tile<64, 1>(key_tile);
@@ -696,7 +743,7 @@ hipError_t launch_score(const ScoreArgs &a, int32_t dtype, int32_t D, int32_t ke
         default: return hipErrorInvalidValue;
         }
     }
-    dim3 grid((unsigned)((a.rows + 7) / 8), (unsigned)((a.clen + kF32Keys - 1) / kF32Keys));
+    const dim3 grid((unsigned)((a.rows + 7) / 8), (unsigned)((a.clen + a.slen - 1) / a.slen));
     const bool two = a.H > 32;
     switch (D) {
     case 32:

@@ -860,7 +860,7 @@ __global__ __launch_bounds__(NT, K <= 2048 ? 4 : 2) void select_kernel(SelectArg
             }
         }
         if (!done) {
-            // No summary (fp32 scores) or massively tied scores.
+            // No summary, or massively tied scores.
             nA = collect_pieces<K>(cand, r, k, bk, sh, tid);
             nB = 0;
         }

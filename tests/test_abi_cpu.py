@@ -76,9 +76,9 @@ def test_key_splits_for_few_rows():
     assert b1 == 64 * 65536 * 4 + 1024 + 64 * 2048 * 8 + 1024
     # Many rows: no splits (same as key_splits=1).
     assert _ws(1 << 14, 1 << 12) == _ws(1 << 14, 1 << 12, key_splits=1)
-    # fp32: never split.
-    assert _ws(64, 1 << 18, q_pos0=(1 << 20) - 64, dtype=torch.float32) == \
-        _ws(64, 1 << 18, q_pos0=(1 << 20) - 64, dtype=torch.float32, key_splits=1)
+    # fp32 plans exactly as bf16 (its kernel writes the same chunk summaries).
+    assert _ws(64, 1 << 18, q_pos0=(1 << 20) - 64, dtype=torch.float32) == b
+    assert _ws(64, 1 << 18, q_pos0=(1 << 20) - 64, dtype=torch.float32, key_splits=1) == b1
 
 
 def test_workspace_tiny_budget_still_fits_one_block():

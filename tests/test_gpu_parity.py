@@ -93,25 +93,25 @@ EDGE_CASES = [
 
 
 @pytest.mark.parametrize("chunk", [0, 1280])
-def test_fp32_several_key_blocks_bit_exact(chunk):
-    """fp32 integer inputs whose rows see about 3,250-3,300 keys: each row's
-    chunk spans several 1,024-key workgroups of the fp32 kernel with a ragged
-    last one, the last query block is ragged (203 rows), and with 1,280-key
-    chunks the running lists are merged across three chunks."""
+def test_fp32_long_rows_bit_exact(chunk):
+    """fp32 integer inputs whose rows see about 3,250-3,300 keys (about a
+    hundred 32-key tiles of the fp32 kernel, the last one ragged), with a
+    ragged last query block (203 rows); with 1,280-key chunks the running
+    lists are merged across three chunks."""
     S, T, H, D, m, k, q_pos0 = 203, 3500, 64, 128, 4, 300, 13000
     q, w, kc = inputs.integer_valued(S, T, H, D, seed=77, dtype=torch.float32, signed_w=True)
-    say("fp32 several key blocks chunk=%d" % chunk)
+    say("fp32 long rows chunk=%d" % chunk)
     g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, chunk_keys=chunk)
     o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
     assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
 
 
-def test_fp32_gaussian_several_key_blocks():
-    """fp32 Gaussian inputs, 1,024 rows that see about 2,000-2,250 keys each
-    (three 1,024-key workgroups per row), by the tolerance rules."""
+def test_fp32_gaussian_long_rows():
+    """fp32 Gaussian inputs, 1,024 rows that see about 2,000-2,250 keys each,
+    by the tolerance rules."""
     S, T, H, D, m, k, q_pos0 = 1024, 4096, 64, 128, 4, 512, 8000
     q, w, kc = inputs.gaussian_fp32(S, T, H, D, seed=5)
-    say("fp32 gaussian several key blocks")
+    say("fp32 gaussian long rows")
     g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
     o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
     fails, stats = checks.check_float(g_idx, g_sc, o_idx, o_sc, q.numpy(), w.numpy(),
@@ -316,15 +316,17 @@ def test_batched_bf16_matches_single_calls_multi_pass():
             assert np.array_equal(s_sc.view(np.uint32), g_sc[b].view(np.uint32))
 
 
-@pytest.mark.parametrize("k", [512, 4096])
-def test_key_splits_integer_bit_exact(k):
+@pytest.mark.parametrize("dtype, k", [(torch.bfloat16, 512), (torch.bfloat16, 4096),
+                                      (torch.float32, 512)])
+def test_key_splits_integer_bit_exact(dtype, k):
     """Few rows against many keys (decode shape): the keys are split, each
     split selects its own best k, the lists are merged pairwise.  Automatic
-    and forced split counts, and several passes, all equal the oracle."""
+    and forced split counts, and several passes, all equal the oracle, for
+    the bf16 and the fp32 score kernels."""
     S, T, H, D, m = 64, 20000, 64, 128, 1
-    q, w, kc = inputs.integer_valued(S, T, H, D, seed=50, dtype=torch.bfloat16, signed_w=True)
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=50, dtype=dtype, signed_w=True)
     q_pos0 = T - 40  # rows see 19961..20000 keys (the last 24 rows all of them)
-    say("key splits integer S=%d T=%d k=%d" % (S, T, k))
+    say("key splits integer S=%d T=%d k=%d %s" % (S, T, k, dtype))
     o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
     for splits, budget in ((0, 0), (1, 0), (2, 0), (16, 0), (64, 0), (4, 1)):
         say("  key_splits=%d budget=%d" % (splits, budget))

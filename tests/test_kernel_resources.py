@@ -73,12 +73,17 @@ def test_score_kernels_no_scratch_and_two_waves_per_simd(score_asm):
                 % tile)
         assert bf16[main]["vgpr_count"] <= 256, main
     # The fp32 path keeps q for up to 64 heads resident (128 registers at
-    # D_I=128) in 8-wave workgroups: no spills, at most 256 registers.
+    # D_I=128) in 8-wave workgroups: no spills, at most 256 registers, and
+    # its tiles plus the 8 row histograms within the CU's 160 KiB of LDS.
     f32 = {n: m for n, m in meta.items() if "score_f32_kernel" in n}
     assert len(f32) == 6
     for name, m in f32.items():
         assert m["vgpr_spill_count"] == 0 and m["private_segment_fixed_size"] == 0, name
         assert m["vgpr_count"] <= 256, name
+    for block in score_asm.split("  - .agpr_count:")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        if "score_f32_kernel" in name:
+            assert int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", block).group(1)) <= 160 * 1024, name
 
 
 def test_select_kernels_no_scratch_on_the_hot_path(select_asm):

@@ -86,6 +86,29 @@ def test_no_entries_at_all(H):
     assert torch.all(out == 0)
 
 
+@pytest.mark.parametrize("H", [32, 64])
+@pytest.mark.parametrize("S, T, k", [(1, 1, 1), (1, 1, 40), (3, 2, 33)])
+def test_smallest_tables(H, S, T, k):
+    """A one- or two-row latent table, one query row or three, with k above
+    T (entries repeat): every selected entry is one of the few rows, some
+    rows padded."""
+    DK, DV = 576, 512
+    say("attention smallest S=%d T=%d k=%d H=%d" % (S, T, k, H))
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=300 + S + T + k + H)
+    idx = random_selection(np.random.default_rng(S + T + k), S, T, k, pad_frac=0.5)
+    run_and_check(q, kv, idx, DV, 1.0 / DK ** 0.5)
+
+
+def test_no_query_rows():
+    """S = 0: an empty output and no launch."""
+    q = torch.empty((0, 64, 576), dtype=torch.bfloat16, device=DEV)
+    kv = torch.zeros((10, 576), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((0, 8), dtype=torch.int32, device=DEV)
+    out = csa.sparse_attention(q, kv, idx, 512)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, 64, 512)
+
+
 @pytest.mark.parametrize("sign", [1.0, -1.0])
 def test_growing_logits_move_the_reference_max(sign):
     """Entries ordered so that the scaled logit rises (by logit for a

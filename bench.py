@@ -39,6 +39,11 @@ METRIC = "scored q-k pairs/s at S=65536 V4-Flash dims; MFMA util %; peak HBM GB"
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_BUSY_PEAK = MFMA_BF16_PEAK_TFLOPS
 HBM_PEAK_GBS = 8000.0
+# Default timed calls: enough for about AUTO_TIMED_MS of timed work in the
+# default run (every other mode takes AUTO_MIN_STEPS unless --steps is given).
+AUTO_TIMED_MS = 2000.0
+AUTO_MIN_STEPS = 20
+AUTO_MAX_STEPS = 500
 # HBM traffic of the score kernel, summarised from two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE) of the default workload by --traffic-from.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_bf16_S65536_hbm_traffic.txt")
@@ -532,7 +537,10 @@ def run_gemm_probe(args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed calls (default: 20; for the default run, enough calls for "
+                         "about %.0f s of timed work, %d to %d)" % (AUTO_TIMED_MS / 1e3,
+                                                                   AUTO_MIN_STEPS, AUTO_MAX_STEPS))
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="workload number 2..5")
     ap.add_argument("--chunk", type=int, default=0)
@@ -578,6 +586,9 @@ def main():
                     help="time a plain library bf16 GEMM (torch.matmul, N x N x N) as a "
                          "reference for the MFMA rate this chip sustains; one JSON line")
     args = ap.parse_args()
+    auto_steps = args.steps is None
+    if auto_steps:
+        args.steps = AUTO_MIN_STEPS
 
     if args.mfma_busy_from:
         sys.stdout.write(summarize_mfma_busy(args.mfma_busy_from, args.kernel_match))
@@ -644,6 +655,16 @@ def main():
     for _ in range(args.warmup):
         csa.topk(q, w, kc, m, k, **kw)
     torch.cuda.synchronize()
+    if auto_steps:
+        # Size K from one more (untimed) call, so that the timed region is
+        # long enough to be seen by a sampling monitor.
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        csa.topk(q, w, kc, m, k, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        est = max(e0.elapsed_time(e1), 1e-3)
+        args.steps = int(min(AUTO_MAX_STEPS, max(AUTO_MIN_STEPS, math.ceil(AUTO_TIMED_MS / est))))
     csa.profile_collect()  # drop anything recorded so far
 
     # The headline: K calls with the library's per-launch events off.  One

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace csa {
 
 // Keys usable by the query at absolute position `pos`: key j is usable iff
@@ -106,6 +108,23 @@ struct MergeArgs {
 
 // Dtype codes as in the public header.
 enum { DT_F32 = 0, DT_BF16 = 1 };
+
+// Raises a kernel's dynamic LDS limit on the current device, once per
+// device: function attributes belong to a device, so `done` holds one bit
+// per device ordinal (devices past 63 set it on every call, which is
+// harmless).
+inline hipError_t set_dynamic_lds(const void *fn, int bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    if (bit) done.fetch_or(bit, std::memory_order_relaxed);
+    return hipSuccess;
+}
 
 // Score kernel (either dtype): grid ceil(rows/8) x splits workgroups, each
 // covering its split of the chunk for its 8 rows; the chunk summary of row r

@@ -637,13 +637,10 @@ hipError_t launch_bf16_cfg(const ScoreArgs &a, hipStream_t s)
                            (size_t)WAVES * kHistBins * sizeof(uint32_t);
     static_assert(lds + (DB ? 2 * (size_t)NT * D * 2 : 0) <= 160 * 1024,
                   "LDS budget of a gfx950 workgroup");
-    static bool attr_set = false;  // benign race: every caller sets the same value
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)score_bf16_kernel<D, HT, NT, DB, WAVES>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> attr_done{0};
+    const hipError_t e =
+        set_dynamic_lds((const void *)score_bf16_kernel<D, HT, NT, DB, WAVES>, (int)lds, attr_done);
+    if (e != hipSuccess) return e;
     const dim3 grid((unsigned)((a.rows + WAVES - 1) / WAVES),
                     (unsigned)((a.clen + a.slen - 1) / a.slen));
     score_bf16_kernel<D, HT, NT, DB, WAVES><<<grid, WAVES * 64, lds, s>>>(a);

@@ -993,14 +993,10 @@ hipError_t launch_merge(const MergeArgs &a, hipStream_t stream)
     const dim3 grid((unsigned)(a.rows * a.half));
     if (a.k <= 2048) {
         if (a.four) {
-            static bool attr_set = false;  // benign race: every caller sets the same value
-            if (!attr_set) {
-                const hipError_t e = hipFuncSetAttribute((const void *)merge4_kernel,
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                         4 * 2048 * (int)sizeof(uint64_t));
-                if (e != hipSuccess) return e;
-                attr_set = true;
-            }
+            static std::atomic<uint64_t> attr_done{0};
+            const hipError_t e = set_dynamic_lds((const void *)merge4_kernel,
+                                                 4 * 2048 * (int)sizeof(uint64_t), attr_done);
+            if (e != hipSuccess) return e;
             merge4_kernel<<<grid, dim3(NT), 4 * 2048 * sizeof(uint64_t), stream>>>(a);
         } else {
             merge_kernel<2048><<<grid, dim3(NT), 2 * 2048 * sizeof(uint64_t), stream>>>(a);
@@ -1018,14 +1014,10 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
     if (a.k <= 2048) {
         select_kernel<2048><<<grid, dim3(NT), Caps<2048>::lds_bytes, stream>>>(a);
     } else {
-        static bool attr_set = false;  // benign race: every caller sets the same value
-        if (!attr_set) {
-            const hipError_t e = hipFuncSetAttribute((const void *)select_kernel<4096>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)Caps<4096>::lds_bytes);
-            if (e != hipSuccess) return e;
-            attr_set = true;
-        }
+        static std::atomic<uint64_t> attr_done{0};
+        const hipError_t e = set_dynamic_lds((const void *)select_kernel<4096>,
+                                             (int)Caps<4096>::lds_bytes, attr_done);
+        if (e != hipSuccess) return e;
         select_kernel<4096><<<grid, dim3(NT), Caps<4096>::lds_bytes, stream>>>(a);
     }
     return hipGetLastError();

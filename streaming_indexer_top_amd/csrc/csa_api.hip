@@ -12,7 +12,8 @@
 // the lists and writes idx/score.  Scratch is R*(4C + 16 [+ 8k + 16]) bytes,
 // set by the workspace and never by S*T.  Problems with few query rows cut
 // one chunk into G key splits instead, run in parallel, each with its own
-// list, and merge the G lists pairwise (R*(4C + G*(16 + 8k + 16)) bytes).
+// list, and merge the G lists in rounds of four (k <= 2048) or two
+// (R*(4C + G*(16 + 8k + 16)) bytes).
 #include <stdint.h>
 #include <string.h>
 

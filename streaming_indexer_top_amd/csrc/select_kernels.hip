@@ -18,7 +18,7 @@
 // (which keys are kept, their order) is taken on these keys, so the outputs
 // are bit-identical for every chunk size.
 //
-// Common path (bf16 scores with the score kernel's histogram summary): the
+// Common path (scores with the score kernel's histogram summary): the
 // summary names the bin b* (top 11 orderable bits) holding the chunk's k-th
 // best key.  One streaming pass sorts each chunk key into "above b*" (all
 // kept, fewer than k), "in b*" (the boundary) or dropped, and appends the kept

@@ -33,8 +33,11 @@
  *   score [S][k]          float32     (4-byte aligned)
  *   workspace             bytes       (256-byte aligned)
  * Outputs are fully overwritten, padding included, and must not overlap the
- * inputs or the workspace.  The library allocates no device memory and keeps
- * no state between calls (apart from the optional profiling counters below).
+ * inputs or the workspace.  The library allocates no device memory at call
+ * time (csa_indexer_topk_noalloc works in a fixed array that is part of the
+ * library's code object on each GPU) and keeps no state between calls that
+ * affects results (apart from that, only the optional profiling counters
+ * below).
  *
  * Asynchrony: all device work is enqueued on `stream` (a hipStream_t; NULL is
  * the default stream) and the call returns without waiting.  Results are

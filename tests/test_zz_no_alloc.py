@@ -68,3 +68,17 @@ def test_noalloc_key_splits_and_chunks():
         got = csa.topk_noalloc(q, w, kc, m, k, q_pos0=q0, **kw)
         torch.cuda.synchronize()
         assert _same(ref, got)
+
+
+def test_noalloc_fp32_inputs():
+    # fp32 inputs (the fp32 score kernel), a decode shape with automatic key
+    # splits and then a multi-chunk row set, each against the workspace call.
+    for S, T, m, k, q0, kw in ((16, 60000, 1, 2048, 59984, {}),
+                               (300, 9000, 1, 700, 8700, dict(chunk_keys=2048))):
+        q, w, kc = inputs.gaussian_fp32(S, T, 64, 128, seed=31, device=DEV)
+        say("noalloc fp32 S=%d T=%d %s" % (S, T, kw))
+        ref = csa.topk(q, w, kc, m, k, q_pos0=q0, **kw)
+        got = csa.topk_noalloc(q, w, kc, m, k, q_pos0=q0, **kw)
+        torch.cuda.synchronize()
+        assert _same(ref, got)
+

@@ -423,17 +423,21 @@ def test_random_configs_bf16_gaussian(case):
     assert_no_fail(fails)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("shape", ["chunks", "key_splits"])
-def test_hip_graph_replays_match_eager(shape):
+def test_hip_graph_replays_match_eager(shape, dtype):
     """The call enqueues only kernel launches on the caller's stream (no
     allocation, no memset), so it can be captured in a HIP graph.  Every
-    replay, with eager work in between, equals the eager result."""
+    replay, with eager work in between, equals the eager result, for the
+    bf16 and the fp32 score kernels."""
     if shape == "chunks":
         S, T, H, D, m, k, q_pos0, kw = 3000, 2500, 64, 128, 4, 512, 0, dict(chunk_keys=256)
     else:
         S, T, H, D, m, k, q_pos0, kw = 16, 60000, 64, 128, 1, 2048, 59984, {}
-    q, w, kc = [t.to(DEV) for t in inputs.bf16_gaussian(S, T, H, D, seed=70)]
-    ws_bytes = csa.workspace_size(S, T, H, D, m, k, q_pos0=q_pos0, **kw)
+    gen = inputs.bf16_gaussian if dtype == "bf16" else inputs.gaussian_fp32
+    q, w, kc = [t.to(DEV) for t in gen(S, T, H, D, seed=70)]
+    say("graph %s %s" % (shape, dtype))
+    ws_bytes = csa.workspace_size(S, T, H, D, m, k, q_pos0=q_pos0, dtype=q.dtype, **kw)
     ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=DEV)
     idx = torch.empty((S, k), dtype=torch.int32, device=DEV)
     sc = torch.empty((S, k), dtype=torch.float32, device=DEV)

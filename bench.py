@@ -665,6 +665,7 @@ def main():
         torch.cuda.synchronize()
         est = max(e0.elapsed_time(e1), 1e-3)
         args.steps = int(min(AUTO_MAX_STEPS, max(AUTO_MIN_STEPS, math.ceil(AUTO_TIMED_MS / est))))
+        args.warmup += 1  # the sizing call is one more untimed call
     csa.profile_collect()  # drop anything recorded so far
 
     # The headline: K calls with the library's per-launch events off.  One

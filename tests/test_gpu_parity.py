@@ -159,6 +159,32 @@ def test_crowded_threshold_bin_is_refined():
     assert_no_fail(fails)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("k", [2048, 4096])
+@pytest.mark.parametrize("values", ["all_zero", "two_values"])
+def test_massively_tied_scores_bit_exact(dtype, k, values):
+    """Rows of about 20,000 keys whose scores take one value (q = 0) or two
+    (every third key scores 1, the rest 0): the boundary bin stays crowded
+    after its refinement, so the select kernel falls back to its piecewise
+    radix select, and the sort's buckets overflow into the bitonic sort.
+    Ties go by index, so the result is unique; it must equal the oracle bit
+    for bit with one chunk, with 4,096-key chunks and with key splits."""
+    S, T, H, D, m = 16, 20000, 4, 32, 1
+    q_pos0 = T - S  # rows see 19,985 .. 20,000 keys
+    q = torch.zeros((S, H, D), dtype=dtype)
+    w = torch.ones((S, H), dtype=dtype)
+    kc = torch.zeros((T, D), dtype=dtype)
+    if values == "two_values":
+        q[:, :, 0] = 1.0
+        kc[::3, 0] = 1.0
+    say("tied scores %s k=%d %s" % (values, k, dtype))
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    for kw in ({}, dict(chunk_keys=4096), dict(key_splits=4)):
+        say("  %s" % kw)
+        g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, **kw)
+        assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
+
+
 def test_signed_zero_scores_are_positive():
     # Every head dot product is <= 0 and the weights are negative: every score
     # is zero and must come out as +0, with ties broken by index.

@@ -109,6 +109,20 @@ def test_no_query_rows():
     assert tuple(out.shape) == (0, 64, 512)
 
 
+def test_nonfinite_queries_stay_in_bounds():
+    """NaN or Inf in some query rows gives those rows unspecified outputs
+    (not detected), but the launch completes and every other row still
+    matches the oracle."""
+    S, T, H, DK, DV, k = 12, 700, 64, 576, 512, 90
+    say("attention non-finite q")
+    q, kv = inputs.attention_gaussian(S, T, H, DK, seed=55)
+    q[0] = float("nan")
+    q[1, 3, 5] = float("inf")
+    q[2, :, 0] = float("-inf")
+    idx = random_selection(np.random.default_rng(55), S, T, k)
+    run_and_check(q, kv, idx, DV, 1.0 / DK ** 0.5, rows=range(3, S))
+
+
 @pytest.mark.parametrize("sign", [1.0, -1.0])
 def test_growing_logits_move_the_reference_max(sign):
     """Entries ordered so that the scaled logit rises (by logit for a

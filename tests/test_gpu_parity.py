@@ -185,6 +185,31 @@ def test_massively_tied_scores_bit_exact(dtype, k, values):
         assert_no_fail(checks.check_exact(g_idx, g_sc, o_idx, o_sc))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_nonfinite_inputs_stay_in_bounds(dtype):
+    """NaN or Inf inputs give unspecified results (the library does not
+    detect them), but the call completes in bounds: rows with finite inputs
+    are still bit-exact, and every row returns min(k, n) distinct usable
+    keys followed by padding."""
+    S, T, H, D, m, k = 24, 6000, 8, 64, 1, 300
+    q_pos0 = T - S
+    q, w, kc = inputs.integer_valued(S, T, H, D, seed=90, dtype=dtype, signed_w=True)
+    q[0:4] = float("nan")            # every score NaN
+    q[4:8, 0, 0] = float("inf")      # +-inf and NaN (inf * 0) logits in head 0
+    w[8:12, 1] = float("-inf")       # an infinite head weight
+    finite = np.arange(12, S)
+    say("non-finite inputs %s" % dtype)
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    o_idx, o_sc = oracle_topk(q, w, kc, m, k, rows=finite, q_pos0=q_pos0)
+    assert_no_fail(checks.check_exact(g_idx[finite], g_sc[finite], o_idx, o_sc))
+    n = oracle.n_valid(np.arange(S) + q_pos0, T, m)
+    for r in range(S):
+        c = int(min(k, n[r]))
+        assert np.all(g_idx[r, :c] >= 0) and np.all(g_idx[r, :c] < n[r]), r
+        assert len(np.unique(g_idx[r, :c])) == c, r
+        assert np.all(g_idx[r, c:] == -1), r
+
+
 def test_signed_zero_scores_are_positive():
     # Every head dot product is <= 0 and the weights are negative: every score
     # is zero and must come out as +0, with ties broken by index.

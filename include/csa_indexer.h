@@ -206,8 +206,9 @@ int csa_indexer_topk_batched(const void *q, const void *w, const void *kc, int32
 
 /*
  * Kernel timing for benchmarks.  While enabled, every kernel launch made by
- * csa_indexer_topk on this process is bracketed by HIP events recorded on the
- * launch's stream.  csa_profile_collect waits for those events, adds up the
+ * the library's entry points (the indexer calls, batched and allocation-free
+ * forms included, and csa_sparse_attention) in this process is bracketed by
+ * HIP events recorded on the launch's stream.  csa_profile_collect waits for those events, adds up the
  * elapsed milliseconds and the launch counts per kernel kind into
  * ms_out[kind] and launches_out[kind] for kind < n_kinds (either array may be
  * NULL), then forgets them.  Not thread-safe; meant for single-threaded

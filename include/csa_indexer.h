@@ -42,7 +42,9 @@
  * Asynchrony: all device work is enqueued on `stream` (a hipStream_t; NULL is
  * the default stream) and the call returns without waiting.  Results are
  * ready when the stream reaches that point.  Asynchronous device faults show
- * up at the caller's next synchronisation, not as a status here.
+ * up at the caller's next synchronisation, not as a status here.  Host
+ * threads may call the library concurrently, each with its own workspace
+ * and outputs (the allocation-free form excepted, see there).
  *
  * Errors: functions return a csa status (0 = CSA_OK).  Every argument check
  * runs before any HIP call, so a call that fails a check enqueues nothing.

@@ -684,3 +684,50 @@ def test_host_or_strided_caller_buffers_are_refused():
     with pytest.raises(ValueError, match="must be on"):
         csa.sparse_attention(qa, kv, ia, 128, out=torch.empty((4, 64, 128), dtype=torch.bfloat16))
     torch.cuda.synchronize()
+
+
+def test_concurrent_calls_from_host_threads():
+    """Calls from several host threads at once, each on its own stream with
+    its own workspace and outputs (the library's shared state is only
+    synchronised bookkeeping), give the results of serial calls bit for
+    bit."""
+    import threading
+    say("concurrent host threads")
+    probs = []
+    for t in range(4):
+        dt = torch.bfloat16 if t % 2 == 0 else torch.float32
+        q, w, kc = [x.to(DEV) for x in inputs.integer_valued(500 + 100 * t, 3000, 64, 128,
+                                                             seed=120 + t, dtype=dt,
+                                                             signed_w=True)]
+        probs.append((q, w, kc, 4, 256 + 64 * t))
+    serial = []
+    for q, w, kc, m, k in probs:
+        serial.append(csa.topk(q, w, kc, m, k))
+    torch.cuda.synchronize()
+    results = [None] * len(probs)
+    errors = []
+
+    def work(i):
+        try:
+            q, w, kc, m, k = probs[i]
+            st = torch.cuda.Stream(device=DEV)
+            with torch.cuda.stream(st):
+                out = None
+                for _ in range(3):
+                    out = csa.topk(q, w, kc, m, k)
+                st.synchronize()
+            results[i] = out
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(probs))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, (a, b) in enumerate(zip(serial, results)):
+        assert torch.equal(a[0], b[0]), i
+        assert torch.equal(a[1].view(torch.int32), b[1].view(torch.int32)), i
+

@@ -105,7 +105,7 @@ typedef struct csa_opts {
      * a long key cache), where chunks alone would leave most of the GPU
      * idle.  0 = automatic (used for fewer than 2048 rows
      * when one pass fits the workspace budget), 1 = never, or a power of two
-     * up to 64. */
+     * up to 128. */
     int32_t key_splits;
     /* Upper bound, in bytes, on the workspace that
      * csa_indexer_topk_workspace_size plans for; 0 means 2 GiB.  A smaller

@@ -45,7 +45,7 @@ constexpr size_t kAlign = 256;
 // reaches twice it, capped by kMaxSplits and by kSplitMinKeys keys per split.
 constexpr int64_t kSplitBlocks = 256;
 constexpr int64_t kSplitMinKeys = 2048;
-constexpr int32_t kMaxSplits = 64;
+constexpr int32_t kMaxSplits = 128;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -255,7 +255,7 @@ const char *csa_status_str(int status)
     case CSA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small for one query block";
     case CSA_ERR_UNSUPPORTED: return "unsupported request: indexer k > 4096 or T >= 2^31; attention dtype, shape or size outside this build";
     case CSA_ERR_HIP: return "HIP call or kernel launch failed";
-    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256 up to 2^24, key_tile one of 64/128/192/256, key_splits 0 or a power of two up to 64, reserved fields 0";
+    case CSA_ERR_BAD_OPTION: return "bad option: chunk_keys must be a multiple of 256 up to 2^24, key_tile one of 64/128/192/256, key_splits 0 or a power of two up to 128, reserved fields 0";
     case CSA_ERR_SCRATCH_TOO_SMALL: return "allocation-free call: one query block needs more scratch than the library's fixed 256 MiB (use a smaller chunk_keys, or csa_indexer_topk with a workspace)";
     default: return "unknown status";
     }

@@ -149,7 +149,7 @@ def test_bad_options():
     lib = csa.load_library()
     for field, val in (("chunk_keys", 100), ("chunk_keys", (1 << 24) + 256), ("key_tile", 96),
                        ("workspace_budget", -1),
-                       ("key_splits", 3), ("key_splits", 128), ("key_splits", -2)):
+                       ("key_splits", 3), ("key_splits", 256), ("key_splits", -2)):
         o = binding.csa_opts()
         setattr(o, field, val)
         assert _call(lib, opts=o) == 8, field

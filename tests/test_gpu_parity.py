@@ -379,7 +379,7 @@ def test_key_splits_integer_bit_exact(dtype, k):
     q_pos0 = T - 40  # rows see 19961..20000 keys (the last 24 rows all of them)
     say("key splits integer S=%d T=%d k=%d %s" % (S, T, k, dtype))
     o_idx, o_sc = oracle_topk(q, w, kc, m, k, q_pos0=q_pos0)
-    for splits, budget in ((0, 0), (1, 0), (2, 0), (16, 0), (64, 0), (4, 1)):
+    for splits, budget in ((0, 0), (1, 0), (2, 0), (16, 0), (64, 0), (128, 0), (4, 1)):
         say("  key_splits=%d budget=%d" % (splits, budget))
         g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0, key_splits=splits,
                                workspace_budget=budget)

@@ -367,11 +367,30 @@ def test_batched_bf16_matches_single_calls_multi_pass():
             assert np.array_equal(s_sc.view(np.uint32), g_sc[b].view(np.uint32))
 
 
+def test_batched_fp32_decode_with_key_splits():
+    """Batched fp32 decode problems (12 rows against 9,000 keys each, so the
+    plan splits the keys): each problem equals the oracle bit for bit and
+    the single call on its slices."""
+    B, S, T, H, D, m, k = 3, 12, 9000, 64, 128, 1, 700
+    probs = [inputs.integer_valued(S, T, H, D, seed=60 + b, dtype=torch.float32, signed_w=True)
+             for b in range(B)]
+    q, w, kc = _stack(probs)
+    q_pos0 = T - S
+    say("batched fp32 decode B=%d S=%d T=%d k=%d" % (B, S, T, k))
+    g_idx, g_sc = gpu_topk(q, w, kc, m, k, q_pos0=q_pos0)
+    for b in range(B):
+        o_idx, o_sc = oracle_topk(*probs[b], m, k, q_pos0=q_pos0)
+        assert_no_fail(checks.check_exact(g_idx[b], g_sc[b], o_idx, o_sc))
+        s_idx, s_sc = gpu_topk(*probs[b], m, k, q_pos0=q_pos0)
+        assert np.array_equal(s_idx, g_idx[b])
+        assert np.array_equal(s_sc.view(np.uint32), g_sc[b].view(np.uint32))
+
+
 @pytest.mark.parametrize("dtype, k", [(torch.bfloat16, 512), (torch.bfloat16, 4096),
                                       (torch.float32, 512)])
 def test_key_splits_integer_bit_exact(dtype, k):
     """Few rows against many keys (decode shape): the keys are split, each
-    split selects its own best k, the lists are merged pairwise.  Automatic
+    split selects its own best k, the lists are merged in rounds.  Automatic
     and forced split counts, and several passes, all equal the oracle, for
     the bf16 and the fp32 score kernels."""
     S, T, H, D, m = 64, 20000, 64, 128, 1
